@@ -1,0 +1,283 @@
+"""Pins for the oracle's estimates, selection and index definitions (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import minference_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, vals = line.split(":")
+            out[int(key)] = [int(x) for x in vals.split()]
+    return out
+
+
+def _rand(seed, n, d):
+    g = np.random.default_rng(seed)
+    return g.standard_normal((n, d)), g.standard_normal((n, d)), g.standard_normal((n, d))
+
+
+# ---------------------------------------------------------------- selection
+
+def test_select_all_equal_takes_lowest_indices():
+    assert list(O.select_topk(np.ones(10), 4)) == [0, 1, 2, 3]
+    assert list(O.select_topk(np.ones(10), 4, {7})) == [0, 1, 2, 7]
+
+
+def test_select_forced_members_always_present():
+    s = np.arange(20, dtype=float)  # index 0 has the lowest score
+    got = O.select_topk(s, 5, {0, 3})
+    assert set(got) >= {0, 3}
+    assert list(got) == [0, 3, 17, 18, 19]
+
+
+def test_select_budget_at_least_candidates_takes_everything():
+    s = np.random.default_rng(0).random(9)
+    assert list(O.select_topk(s, 9)) == list(range(9))
+    assert list(O.select_topk(s, 50, {4})) == list(range(9))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_select_matches_python_sorted_with_ties(seed):
+    g = np.random.default_rng(seed)
+    m = 200
+    s = g.integers(0, 12, m).astype(float)  # heavy ties
+    forced = set(g.choice(m, 3, replace=False).tolist())
+    k = 40
+    rest = sorted((i for i in range(m) if i not in forced), key=lambda i: (-s[i], i))
+    ref = sorted(forced | set(rest[: k - len(forced)]))
+    assert list(O.select_topk(s, k, forced)) == ref
+
+
+def test_select_rejects_more_forced_than_budget():
+    with pytest.raises(ValueError):
+        O.select_topk(np.ones(5), 1, {0, 1})
+
+
+# ---------------------------------------------------------- VS estimate
+
+@pytest.mark.parametrize("n,L", [(64, 64), (130, 16), (257, 64)])
+def test_vs_scores_total_mass(n, L):
+    q, k, _ = _rand(n + L, n, 16)
+    vert, sl = O.vs_estimate(q, k, 0.25, L)
+    assert abs(vert.sum() - L) < 1e-9
+    assert abs(sl.sum() - L) < 1e-9
+    assert (vert >= 0).all() and (sl >= 0).all()
+
+
+def test_vs_scores_closed_form_equal_keys():
+    """All keys equal -> each row spreads uniformly over its causal keys:
+    vertical[j] = sum_r [j <= i_r]/(i_r+1), slash[o] = sum_r [o <= i_r]/(i_r+1)."""
+    n, L, d = 100, 7, 8
+    g = np.random.default_rng(1)
+    q = g.standard_normal((n, d))
+    k = np.tile(g.standard_normal((1, d)), (n, 1))
+    vert, sl = O.vs_estimate(q, k, 0.3, L)
+    rows = np.arange(n - L, n)
+    idx = np.arange(n)
+    ref = ((idx[None, :] <= rows[:, None]) / (rows[:, None] + 1.0)).sum(axis=0)
+    np.testing.assert_allclose(vert, ref, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(sl, ref, atol=1e-13, rtol=0)
+
+
+def test_vs_scores_with_all_queries_are_column_and_diagonal_sums():
+    """L = N: vertical = column sums of the dense causal probability matrix,
+    slash[o] = sum of its o-th subdiagonal (library softmax and trace)."""
+    n, d = 90, 8
+    q, k, _ = _rand(11, n, d)
+    s = torch.from_numpy(0.4 * q @ k.T)
+    s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    p = torch.softmax(s, dim=1).numpy()
+    vert, sl = O.vs_estimate(q, k, 0.4, n)
+    np.testing.assert_allclose(vert, p.sum(axis=0), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(sl, [np.trace(p, offset=-o) for o in range(n)], atol=1e-12, rtol=0)
+
+
+def test_vs_scores_brute_force_loops():
+    n, L, d = 23, 5, 4
+    q, k, _ = _rand(12, n, d)
+    vert, sl = O.vs_estimate(q, k, 0.7, L)
+    bv = [0.0] * n
+    bs = [0.0] * n
+    for r in range(L):
+        i = n - L + r
+        logits = [0.7 * float(q[i] @ k[j]) for j in range(i + 1)]
+        mx = max(logits)
+        ex = [np.exp(x - mx) for x in logits]
+        tot = sum(ex)
+        for j in range(i + 1):
+            bv[j] += ex[j] / tot
+            bs[i - j] += ex[j] / tot
+    np.testing.assert_allclose(vert, bv, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(sl, bs, atol=1e-13, rtol=0)
+
+
+def test_vs_planted_vertical_ranks_first():
+    n, d = 512, 16
+    q, k, _ = _rand(13, n, d)
+    k[300] += 4.0 * q[-16:].mean(axis=0)
+    vert, _ = O.vs_estimate(q, k, 0.25, 16)
+    assert int(np.argmax(vert[:-16])) == 300
+
+
+# ---------------------------------------------------------- VS index
+
+def test_vs_tiles_golden():
+    gold = _read_golden("vs_tiles_b64.txt")
+    S = [0, 1, 64, 130]
+    for a, blocks in gold.items():
+        assert list(O.vs_block_list(a, S, 64)) == blocks
+
+
+@pytest.mark.parametrize("block", [4, 8, 64])
+def test_vs_tiles_closed_form(block):
+    """BL(a) = {a - floor(o/b), a - ceil(o/b) : o in S} ∩ [0, a] (the diagonal of
+    offset o crosses at most two aligned key blocks per query block)."""
+    g = np.random.default_rng(block)
+    nb = 40
+    n = nb * block
+    S = np.unique(np.concatenate([[0], g.choice(n, 25, replace=False)]))
+    for a in range(nb):
+        ref = set()
+        for o in S:
+            for t in (o // block, -(-o // block)):
+                if a - t >= 0:
+                    ref.add(a - t)
+        assert list(O.vs_block_list(a, S, block)) == sorted(ref)
+
+
+def test_vs_index_full_budget_is_dense():
+    n, d = 64 * 4, 8
+    q, k, v = _rand(14, n, d)
+    idx = O.HeadIndex(O.VSLASH, n, V=np.arange(n), S=np.arange(n))
+    dense, dlse = O.dense_causal_attention(q, k, v, 0.3)
+    out = O.head_attention(q, k, v, 0.3, idx, range(4))
+    for a in range(4):
+        np.testing.assert_allclose(out[a][0], dense[64 * a: 64 * a + 64], atol=1e-12, rtol=0)
+        assert len(idx.cols(a)) == 0  # every vertical lies in a listed tile
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_vs_index_invariants(seed):
+    g = np.random.default_rng(seed)
+    n = 64 * 12
+    V = np.unique(np.concatenate([[0], g.choice(n, 30, replace=False)]))
+    S = np.unique(np.concatenate([[0], g.choice(n, 20, replace=False)]))
+    for a in range(12):
+        bl = O.vs_block_list(a, S)
+        cl = O.vs_column_list(a, V, bl)
+        assert a in bl  # offset 0 -> diagonal tile
+        assert 0 in np.unique(np.concatenate([bl, cl // 64]))  # the sink key is reachable
+        assert not np.isin(cl // 64, bl).any()  # no key counted twice
+        assert np.isin(cl, V).all()
+        u = O.block_union(bl, cl)
+        for i in range(64 * a, 64 * a + 64):
+            exact = O.vs_exact_allowed(i, V, S)
+            assert np.isin(exact, u).all()  # exact VS keys are all computed
+            assert i in u
+
+
+# ---------------------------------------------------------- Block-Sparse
+
+def test_bs_block_size_one_is_per_token_topk():
+    n, d = 40, 8
+    q, k, _ = _rand(15, n, d)
+    w, kept = O.bs_estimate(q, k, 0.5, 6, block=1)
+    logits = 0.5 * q @ k.T
+    for a in range(n):
+        ref = O.select_topk(logits[a, : a + 1], min(6, a + 1), {0, a})
+        assert list(kept[a]) == list(ref)
+        np.testing.assert_allclose(w[a, : a + 1].sum(), 1.0, atol=1e-13)
+        assert (w[a, a + 1:] == 0).all()
+
+
+def test_bs_means_of_constant_blocks():
+    d = 4
+    k = np.repeat(np.arange(3 * d, dtype=float).reshape(3, d), 64, axis=0)
+    np.testing.assert_array_equal(O.block_means(k), k[::64])
+    x = np.arange(128 * 2, dtype=float).reshape(128, 2)
+    np.testing.assert_allclose(O.block_means(x), [[63.0, 64.0], [191.0, 192.0]])
+
+
+def test_bs_full_budget_is_dense():
+    n, d = 64 * 5, 8
+    q, k, v = _rand(16, n, d)
+    _, kept = O.bs_estimate(q, k, 0.3, 100)
+    idx = O.HeadIndex(O.BSPARSE, n, kept=kept)
+    dense, _ = O.dense_causal_attention(q, k, v, 0.3)
+    out = O.head_attention(q, k, v, 0.3, idx, range(5))
+    for a in range(5):
+        assert list(kept[a]) == list(range(a + 1))
+        np.testing.assert_allclose(out[a][0], dense[64 * a: 64 * a + 64], atol=1e-12, rtol=0)
+
+
+def test_bs_row_sizes_and_forced_blocks():
+    n, d = 64 * 9, 8
+    q, k, _ = _rand(17, n, d)
+    _, kept = O.bs_estimate(q, k, 0.3, 4)
+    for a in range(9):
+        kb = kept[a]
+        assert len(kb) == min(4, a + 1)
+        assert 0 in kb and a in kb
+        u = O.block_union(kb, [])
+        for r in (0, 17, 63):
+            i = 64 * a + r
+            assert (u <= i).sum() == 64 * (len(kb) - 1) + r + 1
+
+
+# ---------------------------------------------------------- A-shape
+
+def test_ashape_golden():
+    gold = _read_golden("ashape_n8_s2_w3.txt")
+    for i, keys in gold.items():
+        assert list(O.ashape_allowed(i, 2, 3)) == keys
+
+
+@pytest.mark.parametrize("s,w", [(2, 3), (128, 4096), (5, 64), (0, 1)])
+def test_ashape_row_sizes(s, w):
+    for i in list(range(0, 300, 7)) + [5000]:
+        size = len(O.ashape_allowed(i, s, w))
+        assert size == (i + 1 if i + 1 <= s + w else s + w)
+
+
+def test_ashape_covering_window_is_dense():
+    n, d = 64 * 3, 8
+    q, k, v = _rand(18, n, d)
+    dense, _ = O.dense_causal_attention(q, k, v, 0.3)
+    idx = O.HeadIndex(O.ASHAPE, n, sink=10, local=n - 10)
+    out = O.head_attention(q, k, v, 0.3, idx, range(3))
+    for a in range(3):
+        np.testing.assert_allclose(out[a][0], dense[64 * a: 64 * a + 64], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("s,w", [(128, 4096), (100, 300), (3, 70)])
+def test_ashape_block_attention_matches_row_gather(s, w):
+    n, d = 64 * 10, 8
+    q, k, v = _rand(19, n, d)
+    for a in (0, 1, 5, 9):
+        rows = np.arange(64 * a, 64 * a + 64)
+        o, lse = O.ashape_attention(q, k, v, 0.3, rows, s, w)
+        for r, i in enumerate(rows):
+            oi, li = O.attention_row_gather(q, k, v, 0.3, i, O.ashape_allowed(i, s, w))
+            np.testing.assert_allclose(o[r], oi, atol=1e-12, rtol=0)
+            assert abs(lse[r] - li) < 1e-12
+
+
+@pytest.mark.parametrize("s,w", [(128, 4096), (100, 300), (3, 70), (64, 64)])
+def test_ashape_block_list_closed_form(s, w):
+    """Key block c <= a is touched iff it holds a sink key (64c < s) or its
+    nearest key pair is inside the window (64(a-c) - 63 < w)."""
+    n = 64 * 80
+    for a in (0, 1, 2, 10, 64, 65, 79):
+        ref = [c for c in range(a + 1) if 64 * c < s or 64 * (a - c) - 63 < w]
+        assert list(O.ashape_block_list(a, s, w, n)) == ref
