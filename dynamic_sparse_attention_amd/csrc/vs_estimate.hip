@@ -1,0 +1,316 @@
+// Vertical-Slash estimate for gfx950: the last last_q queries of a head
+// against every key, causal softmax per row, then column sums (vertical
+// scores) and diagonal sums (slash scores).  hotpaper.ai summary of arXiv
+// 2407.02490, key idea: Vertical-Slash heads estimate their important
+// positions from the last last_q queries.
+//
+// Three launches, all over (batch, listed head, key chunk):
+//   1. rowstat_partial: per 1024-key chunk, each row's running max and
+//      normaliser (log2 domain) with bf16/fp32 MFMA scores;
+//   2. rowstat_combine: merges the chunk partials of each row in a fixed
+//      order;
+//   3. scores: recomputes the scores of a chunk of keys, normalises them with
+//      the row statistics, stores the 64 x (C+64) probabilities in LDS and
+//      sums columns and diagonals.  Work item c owns slash offsets
+//      [cC, cC+C) and vertical keys [N-(c+1)C, N-cC); the diagonals of those
+//      offsets reach keys [N-(c+1)C-63, N-cC), so each item recomputes 64
+//      extra keys instead of exchanging partial sums.  Every output is written
+//      by one thread with a fixed summation order (deterministic).
+//
+// Score layout (MFMA result, transposed): S^T (32 keys x 32 rows) = K . Q^T.
+// Lane l holds query row (l%32) of row block rb and keys
+// 8*(e/4) + 4*(l/32) + (e%4) of the 32-key unit.
+#include "mi_device.h"
+#include "mi_internal.h"
+
+namespace mi {
+namespace {
+
+constexpr int kChunk1 = 1024;  // keys per row-statistics work item
+constexpr int kChunk2 = 256;   // offsets (and vertical keys) per score work item
+constexpr int kPitch2 = kChunk2 + 64 + 4;  // LDS row pitch of the probability tile (floats)
+
+struct VsP {
+    const char* q;
+    const char* k;
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+    int32_t B, Hq, N, group, n_heads, last_q;
+    float c;  // scale * log2(e)
+    int32_t heads[MI_MAX_HEADS];
+    float* stats;    // [B*n_heads][nchunk1][64] x (m, l)
+    float* rowstat;  // [B*n_heads][64] x (m, l)
+    int32_t nchunk1, nchunk2;
+    float* vscore;
+    float* sscore;
+    int64_t srow_b, srow_h;  // score row strides (elements)
+    int32_t score_by_head;   // 1: row index is the head id, 0: the list position
+};
+
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
+    m = M;
+}
+
+// Q fragments of the estimate rows: row slot r = 32*rb + (l%32) holds query
+// i_r = N - last_q + r (zero for r >= last_q).
+template <typename T, int D>
+__device__ __forceinline__ void load_q_rows(const VsP& p, const T* qbase, int rl, int hl,
+                                            typename Elem<T>::frag (&qf)[2][D / 16]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = rb * 32 + rl;
+        if (r < p.last_q) {
+            const T* qrow = qbase + (int64_t)(p.N - p.last_q + r) * p.qs2;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) qf[rb][s] = load_frag(qrow + 16 * s + 8 * hl);
+        } else {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) qf[rb][s] = typename Elem<T>::frag{};
+        }
+    }
+}
+
+// Scores of 32 keys [key0, key0+32) against the 64 row slots.  Keys outside
+// [0, N) contribute zero fragments (the caller masks them).
+template <typename T, int D>
+__device__ __forceinline__ void unit_scores(const VsP& p, const T* kbase, int key0, int rl, int hl,
+                                            const typename Elem<T>::frag (&qf)[2][D / 16],
+                                            f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+    const int key = key0 + rl;
+    const bool ok = key >= 0 && key < p.N;
+    const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        typename Elem<T>::frag kf = ok ? load_frag(krow + 16 * s) : typename Elem<T>::frag{};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf, qf[rb][s]);
+    }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
+    const int nitems = p.B * p.n_heads * p.nchunk1;
+    const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.group);
+    if (L >= nitems) return;
+    // consecutive items: same chunk, consecutive listed heads (shared K in L2)
+    const int chunk = L / (p.B * p.n_heads);
+    const int bl = L % (p.B * p.n_heads);
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li], kvh = h / p.group;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rl = lane & 31, hl = lane >> 5;
+    const T* qbase = reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1;
+    const T* kbase = reinterpret_cast<const T*>(p.k) + b * p.ks0 + kvh * p.ks1;
+
+    typename Elem<T>::frag qf[2][D / 16];
+    load_q_rows<T, D>(p, qbase, rl, hl, qf);
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int u = wave; u < kChunk1 / 32; u += 4) {
+        const int key0 = chunk * kChunk1 + u * 32;
+        if (key0 >= p.N) break;
+        f32x16 acc[2];
+        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int r = rb * 32 + rl;
+            const int ir = p.N - p.last_q + r;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+                const float s = (r < p.last_q && j <= ir) ? acc[rb][e] * p.c : -INFINITY;
+                acc[rb][e] = s;
+                mx = fmaxf(mx, s);
+            }
+            const float M = fmaxf(m[rb], mx);
+            if (M == -INFINITY) continue;
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sum += fast_exp2(acc[rb][e] - M);
+            l[rb] = l[rb] * fast_exp2(m[rb] - M) + sum;
+            m[rb] = M;
+        }
+    }
+    // lane pair (l, l^32) share a row; then 4 waves through LDS
+    __shared__ float sm_m[4][64], sm_l[4][64];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        merge_ml(m[rb], l[rb], swap32(m[rb]), swap32(l[rb]));
+        if (hl == 0) {
+            sm_m[wave][rb * 32 + rl] = m[rb];
+            sm_l[wave][rb * 32 + rl] = l[rb];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int r = threadIdx.x;
+        float M = sm_m[0][r], Ls = sm_l[0][r];
+        for (int w = 1; w < 4; ++w) merge_ml(M, Ls, sm_m[w][r], sm_l[w][r]);
+        float* out = p.stats + (((int64_t)bl * p.nchunk1 + chunk) * 64 + r) * 2;
+        out[0] = M;
+        out[1] = Ls;
+    }
+}
+
+__global__ void __launch_bounds__(64) vs_rowstat_combine(VsP p) {
+    const int bl = blockIdx.x;
+    const int r = threadIdx.x;
+    float M = -INFINITY, Ls = 0.f;
+    const float* in = p.stats + ((int64_t)bl * p.nchunk1 * 64 + r) * 2;
+    for (int c = 0; c < p.nchunk1; ++c) merge_ml(M, Ls, in[(int64_t)c * 128], in[(int64_t)c * 128 + 1]);
+    p.rowstat[((int64_t)bl * 64 + r) * 2] = M;
+    p.rowstat[((int64_t)bl * 64 + r) * 2 + 1] = Ls;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) vs_scores(VsP p) {
+    __shared__ float P[64 * kPitch2];
+    const int nitems = p.B * p.n_heads * p.nchunk2;
+    const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.group);
+    if (L >= nitems) return;
+    const int chunk = L / (p.B * p.n_heads);
+    const int bl = L % (p.B * p.n_heads);
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li], kvh = h / p.group;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rl = lane & 31, hl = lane >> 5;
+    const T* qbase = reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1;
+    const T* kbase = reinterpret_cast<const T*>(p.k) + b * p.ks0 + kvh * p.ks1;
+
+    typename Elem<T>::frag qf[2][D / 16];
+    load_q_rows<T, D>(p, qbase, rl, hl, qf);
+    float mrow[2], inv_l[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float* rs = p.rowstat + ((int64_t)bl * 64 + rb * 32 + rl) * 2;
+        mrow[rb] = rs[0];
+        inv_l[rb] = rs[1] > 0.f ? 1.f / rs[1] : 0.f;
+    }
+
+    const int J0 = p.N - chunk * kChunk2 - kChunk2 - 64;  // first key of the tile
+    for (int u = wave; u < (kChunk2 + 64) / 32; u += 4) {
+        const int key0 = J0 + u * 32;
+        f32x16 acc[2];
+        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int r = rb * 32 + rl;
+            const int ir = p.N - p.last_q + r;
+            float pv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+                const bool ok = (r < p.last_q) && (j >= 0) && (j <= ir);
+                pv[e] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
+            }
+            float* dst = &P[r * kPitch2 + u * 32 + 4 * hl];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<f32x4*>(dst + 8 * q4) =
+                    f32x4{pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;  // kChunk2 == blockDim
+    float* vrow = p.vscore + b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
+    float* srow = p.sscore + b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
+    const int j = J0 + 64 + t;
+    if (j >= 0) {
+        float acc = 0.f;
+        for (int r = 0; r < p.last_q; ++r) acc += P[r * kPitch2 + 64 + t];
+        vrow[j] = acc;
+    }
+    const int o = chunk * kChunk2 + t;
+    if (o < p.N) {
+        float acc = 0.f;
+        const int base = kChunk2 + 64 - p.last_q - t;
+        for (int r = 0; r < p.last_q; ++r) acc += P[r * kPitch2 + base + r];
+        srow[o] = acc;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(VsP& p, hipStream_t s) {
+    const int n1 = p.B * p.n_heads * p.nchunk1;
+    hipLaunchKernelGGL((vs_rowstat_partial<T, D>), dim3(n1), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(vs_rowstat_combine, dim3(p.B * p.n_heads), dim3(64), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n2 = p.B * p.n_heads * p.nchunk2;
+    hipLaunchKernelGGL((vs_scores<T, D>), dim3(n2), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t vs_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_scores) {
+    const size_t nchunk1 = (N + kChunk1 - 1) / kChunk1;
+    size_t bytes = align256((size_t)B * n_heads * nchunk1 * 64 * 2 * sizeof(float));
+    bytes += align256((size_t)B * n_heads * 64 * 2 * sizeof(float));
+    if (!caller_scores) bytes += 2 * align256((size_t)B * n_heads * N * sizeof(float));
+    return bytes;
+}
+
+hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
+    VsP p{};
+    p.q = static_cast<const char*>(a.q);
+    p.k = static_cast<const char*>(a.k);
+    p.qs0 = a.qs[0]; p.qs1 = a.qs[1]; p.qs2 = a.qs[2];
+    p.ks0 = a.ks[0]; p.ks1 = a.ks[1]; p.ks2 = a.ks[2];
+    p.B = a.B; p.Hq = a.Hq; p.N = a.N; p.group = a.Hq / a.Hkv;
+    p.n_heads = a.n_heads; p.last_q = a.last_q;
+    p.c = a.scale * kLog2e;
+    for (int i = 0; i < a.n_heads; ++i) p.heads[i] = a.heads[i];
+    p.nchunk1 = (a.N + kChunk1 - 1) / kChunk1;
+    p.nchunk2 = (a.N + kChunk2 - 1) / kChunk2;
+    char* ws = static_cast<char*>(a.ws);
+    size_t off = 0;
+    p.stats = reinterpret_cast<float*>(ws + off);
+    off += align256((size_t)a.B * a.n_heads * p.nchunk1 * 64 * 2 * sizeof(float));
+    p.rowstat = reinterpret_cast<float*>(ws + off);
+    off += align256((size_t)a.B * a.n_heads * 64 * 2 * sizeof(float));
+    if (a.vscore != nullptr) {
+        // caller rows [B, Hq, N], indexed by head id
+        p.vscore = a.vscore;
+        p.sscore = a.sscore;
+        p.srow_b = (int64_t)a.Hq * a.N;
+        p.srow_h = a.N;
+        p.score_by_head = 1;
+    } else {
+        // workspace rows [B, n_heads, N], indexed by list position
+        p.vscore = reinterpret_cast<float*>(ws + off);
+        off += align256((size_t)a.B * a.n_heads * a.N * sizeof(float));
+        p.sscore = reinterpret_cast<float*>(ws + off);
+        p.srow_b = (int64_t)a.n_heads * a.N;
+        p.srow_h = a.N;
+        p.score_by_head = 0;
+    }
+    hipError_t e;
+    if (a.dtype == MI_BF16)
+        e = a.D == 128 ? launch_t<uint16_t, 128>(p, s) : launch_t<uint16_t, 64>(p, s);
+    else
+        e = a.D == 128 ? launch_t<float, 128>(p, s) : launch_t<float, 64>(p, s);
+    if (e != hipSuccess) return e;
+    // top-k over both score rows of every listed head
+    TopkRows t{};
+    t.B = a.B; t.Hq = a.Hq; t.n_heads = a.n_heads; t.n = a.N;
+    for (int i = 0; i < a.n_heads; ++i) t.heads[i] = a.heads[i];
+    t.score_by_head = p.score_by_head;
+    t.srow_b = p.srow_b; t.srow_h = p.srow_h;
+    t.list[0] = {p.vscore, a.vertical_idx, a.n_vertical, a.force_vertical};
+    t.list[1] = {p.sscore, a.slash_idx, a.n_slash, a.force_slash};
+    return launch_topk_rows(t, s);
+}
+
+}  // namespace mi

@@ -1,0 +1,216 @@
+/*
+ * mi_sparse.h -- C ABI of an MI355X (gfx950) library for MInference-style
+ * dynamic sparse prefill attention.
+ *
+ * The method (arXiv 2407.02490, "MInference 1.0: Accelerating Pre-filling for
+ * Long-Context LLMs via Dynamic Sparse Attention", abstract): every attention
+ * head is assigned offline to one of three sparse patterns -- A-shape,
+ * Vertical-Slash, Block-Sparse -- and at prefill time a sparse index is built
+ * online from the input for that pattern, then attention runs only on the
+ * indexed keys.  The four compute entry points below are the stages of that
+ * path: two online estimates, the conversion of their output into per-query-
+ * block work lists, and the sparse attention itself.
+ *
+ * Conventions for every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; it enqueues kernels on `stream`
+ *    (a hipStream_t; NULL means the default stream) and returns.
+ *  - Small arrays documented as HOST arrays (`heads`, `head_pattern`) are read
+ *    during the call and copied by value into kernel arguments.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error the call returns a non-zero mi_status, enqueues nothing and leaves
+ *    every output untouched; mi_last_error() then holds a one-line reason for
+ *    the calling thread.  MI_ERR_LAUNCH reports a failed kernel launch (work
+ *    enqueued before it may have run).  Faults inside kernels surface at the
+ *    caller's next synchronisation, as with any HIP kernel.
+ *  - Calls are stateless and re-entrant.  Two calls that write the same output
+ *    or workspace on different streams race; nothing else is shared.
+ *  - Token block size is fixed at 64 (MI_BLOCK): seq_len must be a multiple of
+ *    64.  Query block a holds query rows [64a, 64a+64); nb = seq_len / 64.
+ *  - Tensors Q, K, V, O are laid out [batch, head, token, head_dim] with
+ *    head_dim contiguous and arbitrary element strides for (batch, head, token)
+ *    given in mi_attn_desc.  Query head h reads key/value head
+ *    h / (heads_q / heads_kv) (grouped-query attention).
+ */
+#ifndef MI_SPARSE_H
+#define MI_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_BLOCK 64
+#define MI_MAX_HEADS 256
+
+typedef enum {
+    MI_OK = 0,
+    MI_ERR_NULL = 1,      /* a required pointer is NULL */
+    MI_ERR_SHAPE = 2,     /* unsupported size, stride or alignment */
+    MI_ERR_BUDGET = 3,    /* a budget, forced count or list capacity is out of range */
+    MI_ERR_DTYPE = 4,     /* unknown dtype */
+    MI_ERR_WORKSPACE = 5, /* workspace smaller than mi_workspace_bytes() */
+    MI_ERR_LAUNCH = 6,    /* a kernel launch failed */
+    MI_ERR_PATTERN = 7    /* bad head list or pattern code */
+} mi_status;
+
+typedef enum { MI_F32 = 0, MI_BF16 = 1 } mi_dtype;
+
+/* Per-head pattern codes.  MI_DENSE (plain causal attention) is not one of the
+ * method's patterns; it is the comparator the sparse kernel is measured
+ * against and a safe choice for heads that fit no pattern. */
+typedef enum { MI_ASHAPE = 0, MI_VSLASH = 1, MI_BSPARSE = 2, MI_DENSE = 3 } mi_pattern;
+
+/* Workspace-sized operations for mi_workspace_bytes(). */
+typedef enum { MI_OP_VS_ESTIMATE = 0, MI_OP_BLOCK_ESTIMATE = 1, MI_OP_SPARSE_PREFILL = 2 } mi_op;
+
+typedef struct {
+    int32_t batch, heads_q, heads_kv, seq_len, head_dim; /* head_dim in {64, 128} */
+    int32_t dtype;        /* mi_dtype of Q, K, V and O (f32 or bf16) */
+    float scale;          /* softmax scale applied to q.k, normally 1/sqrt(head_dim) */
+    int64_t q_stride[3];  /* element strides of (batch, head, token); head_dim contiguous */
+    int64_t k_stride[3];  /* strides must be multiples of 8 elements (16-byte rows) */
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+} mi_attn_desc;
+
+/* Per-query-block work lists (device memory, caller-owned).
+ *   block_count [batch, heads_q, nb]             number of key blocks of query block a
+ *   block_idx   [batch, heads_q, nb, block_cap]  key-block ids, ascending, padded with -1
+ *   col_count   [batch, heads_q, nb]             number of gathered key columns
+ *   col_idx     [batch, heads_q, nb, col_cap]    key positions, ascending, padded with -1
+ * Query block a of a head attends, for each row i, to the keys j <= i that lie
+ * in a listed key block or are listed columns.  A listed column never lies in
+ * a listed key block. */
+typedef struct {
+    int32_t* block_count;
+    int32_t* block_idx;
+    int32_t* col_count;
+    int32_t* col_idx;
+    int32_t block_cap;
+    int32_t col_cap;
+} mi_index;
+
+/* Bytes of workspace an operation needs.  op = MI_OP_VS_ESTIMATE: p0 = number
+ * of listed heads; MI_OP_BLOCK_ESTIMATE: p0 = number of listed heads;
+ * MI_OP_SPARSE_PREFILL: 0 (no workspace).  Returns 0 for an invalid desc. */
+size_t mi_workspace_bytes(const mi_attn_desc* desc, int32_t op, int32_t p0, int32_t p1);
+
+/* Vertical-Slash index estimate (hotpaper.ai summary of arXiv 2407.02490, key
+ * idea: Vertical-Slash heads use the last last_q queries against the keys to
+ * find globally important positions; aifetchly guide, "The Vertical-Slash
+ * Pattern": vertical lines are keys every later query attends to, slash lines
+ * are fixed offsets o = i - j).
+ *
+ * For each listed query head h and batch b, with rows i_r = N - last_q + r:
+ *   P[r, j]       = softmax over keys j <= i_r of scale * q_{i_r} . k_j
+ *   vertical[j]   = sum_r P[r, j]            j in [0, N)
+ *   slash[o]      = sum_r P[r, i_r - o]      o in [0, N), terms i_r - o < 0 omitted
+ *   vertical_idx  = {0..force_vertical-1} plus the highest-scoring other keys,
+ *                   n_vertical in total (clamped to N), ascending
+ *   slash_idx     = {0..force_slash-1} plus the highest-scoring other offsets,
+ *                   n_slash in total (clamped to N), ascending
+ * Equal scores rank the lower index first.  Selection uses the fp32 scores as
+ * written to vertical_score / slash_score.
+ *   heads          HOST int32[n_heads], strictly increasing q-head ids
+ *   vertical_idx   int32 [batch, heads_q, n_vertical]; rows of listed heads written,
+ *                  entries beyond the clamped budget set to -1
+ *   slash_idx      int32 [batch, heads_q, n_slash], likewise
+ *   vertical_score float [batch, heads_q, seq_len] or NULL (then kept in ws)
+ *   slash_score    float [batch, heads_q, seq_len] or NULL
+ *   ws             >= mi_workspace_bytes(desc, MI_OP_VS_ESTIMATE, n_heads, 0) bytes
+ * Requires 1 <= last_q <= 64, last_q <= seq_len, 1 <= force_vertical <=
+ * n_vertical and 1 <= force_slash <= n_slash. */
+mi_status mi_vs_estimate(const mi_attn_desc* desc, const void* q, const void* k,
+                         const int32_t* heads, int32_t n_heads, int32_t last_q,
+                         int32_t n_vertical, int32_t n_slash,
+                         int32_t force_vertical, int32_t force_slash,
+                         int32_t* vertical_idx, int32_t* slash_idx,
+                         float* vertical_score, float* slash_score,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Block-Sparse index estimate (hotpaper.ai summary, key idea: 64-token mean
+ * pooling gives block-level attention weights; aifetchly guide, "2. The
+ * Block-Sparse Kernel Mechanics": mean key of each 64-token block, dot products
+ * with the query block, top-k key blocks kept).
+ *
+ * For each listed query head h and batch b, with Qbar_a, Kbar_c the fp32 means
+ * of the 64 query rows of block a and the 64 key rows of block c:
+ *   z[a, c] = scale * Qbar_a . Kbar_c for c <= a
+ *   w[a, c] = softmax over c <= a of z[a, c];  w[a, c] = 0 for c > a
+ *   block_idx[a] = {0, a} plus the highest-weight other blocks c <= a,
+ *                  min(top_blocks, a + 1) in total, ascending, padded with -1
+ *   heads        HOST int32[n_heads], strictly increasing q-head ids
+ *   block_idx    int32 [batch, heads_q, nb, top_blocks]
+ *   block_count  int32 [batch, heads_q, nb]
+ *   block_score  float [batch, heads_q, nb, nb] (w) or NULL (then kept in ws)
+ *   ws           >= mi_workspace_bytes(desc, MI_OP_BLOCK_ESTIMATE, n_heads, 0)
+ * Requires top_blocks >= 2.  Equal weights rank the lower block first. */
+mi_status mi_block_estimate(const mi_attn_desc* desc, const void* q, const void* k,
+                            const int32_t* heads, int32_t n_heads, int32_t top_blocks,
+                            int32_t* block_idx, int32_t* block_count, float* block_score,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Conversion of the estimates into per-query-block work lists (aifetchly
+ * guide, "1. The Vertical-Slash Kernel Mechanics": verticals are read as
+ * coalesced chunks; "2. The Block-Sparse Kernel Mechanics": only active
+ * 64x64 tiles run on the matrix units).  Writes `out` for every head, by
+ * head_pattern[h] (HOST int32[heads_q]):
+ *   MI_VSLASH : slash offsets S (slash_idx row, -1 entries ignored) become the
+ *               tile distances T = {floor(o/64), ceil(o/64) : o in S};
+ *               block list of a = {a - t : t in T, t <= a};
+ *               column list of a = {j in V : j <= 64a + 63, block of j not
+ *               listed}, V = vertical_idx row.
+ *   MI_BSPARSE: block list = bs_block_idx[b, h, a, :bs_block_count], no columns.
+ *   MI_ASHAPE : block list = key blocks c <= a holding a sink key (64c <
+ *               sink_tokens) or within the local window of some row
+ *               (64(a - c) - 63 < local_tokens); no columns.
+ *   MI_DENSE  : block_count = a + 1, col_count = 0, lists not written (the
+ *               attention treats dense heads as all causal blocks).
+ * Pointers for patterns no head uses may be NULL.  Capacities: block_cap >=
+ * min(nb, 2 n_slash) if any VS head, >= top_blocks if any BS head, >= the
+ * A-shape maximum min(nb, ceil(sink/64) + floor((local + 126)/64)) if any
+ * A-shape head; col_cap >= min(n_vertical, seq_len) if any VS head. */
+mi_status mi_build_index(const mi_attn_desc* desc, const int32_t* head_pattern,
+                         const int32_t* vertical_idx, int32_t n_vertical,
+                         const int32_t* slash_idx, int32_t n_slash,
+                         const int32_t* bs_block_idx, const int32_t* bs_block_count,
+                         int32_t top_blocks, int32_t sink_tokens, int32_t local_tokens,
+                         const mi_index* out, void* stream);
+
+/* Sparse prefill attention (arXiv 2407.02490 abstract: sparse attention with
+ * the per-head pattern and online index; aifetchly guide, "1. The
+ * Vertical-Slash Kernel Mechanics": online softmax keeps a running max and
+ * normaliser so no score matrix is written).
+ *
+ * For each batch b, query head h and row i:
+ *   o_i = sum_{j in A(i)} softmax_j(scale * q_i . k_j) v_j
+ *   lse_i = log sum_{j in A(i)} exp(scale * q_i . k_j)      (natural log)
+ * with A(i) from head h's pattern:
+ *   MI_VSLASH, MI_BSPARSE: keys j <= i in the listed blocks or listed columns of
+ *                          the row's query block (idx);
+ *   MI_ASHAPE: keys j <= i with j < sink_tokens or i - j < local_tokens (idx
+ *              holds the block list; edges are masked per element);
+ *   MI_DENSE : all keys j <= i (idx not read).
+ * head_pattern == NULL runs every head as MI_DENSE (the dense comparator; idx
+ * may then be NULL).  O is written in desc->dtype; bf16 inputs use bf16 MFMA
+ * with fp32 softmax and accumulation, f32 inputs use fp32 MFMA.
+ *   o    [batch, heads_q, seq_len, head_dim] with desc->o_stride
+ *   lse  float [batch, heads_q, seq_len] or NULL */
+mi_status mi_sparse_prefill(const mi_attn_desc* desc, const void* q, const void* k,
+                            const void* v, const int32_t* head_pattern, const mi_index* idx,
+                            int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Static text of a status code. */
+const char* mi_status_str(mi_status s);
+
+/* Reason for the last non-MI_OK status returned on the calling thread. */
+const char* mi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI_SPARSE_H */

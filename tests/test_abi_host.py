@@ -1,0 +1,156 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, and rejects bad arguments before enqueuing anything.
+
+No kernel is launched here: every call below fails validation, which runs
+before any HIP call, so fake (never dereferenced) device addresses are used.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_amd as mi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mi_sparse.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:mi_status|size_t|const char\*)\s+(mi_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(mi.EXPORTS)
+    l = mi.lib()
+    for n in names:
+        assert hasattr(l, n), n
+
+
+def test_status_strings():
+    l = mi.lib()
+    for code in range(8):
+        assert l.mi_status_str(code)
+    assert l.mi_status_str(99) == b"unknown status"
+
+
+def desc(**kw):
+    d = mi.MiAttnDesc()
+    d.batch, d.heads_q, d.heads_kv, d.seq_len, d.head_dim = 1, 4, 2, 1024, 128
+    d.dtype, d.scale = mi.MI_BF16, 128 ** -0.5
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(d, name)[:] = (4 * 1024 * 128, 1024 * 128, 128)
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(d, k)[:] = v
+        else:
+            setattr(d, k, v)
+    return d
+
+
+def heads(*h):
+    return ctypes.cast((ctypes.c_int32 * len(h))(*h), ctypes.c_void_p)
+
+
+def vs_call(d, hs=(0, 1), n_heads=None, last_q=64, nv=16, ns=32, fv=1, fs=1, ws=FAKE, ws_bytes=1 << 30,
+            vidx=FAKE, sidx=FAKE, q=FAKE, vsc=None, ssc=None):
+    l = mi.lib()
+    return l.mi_vs_estimate(ctypes.byref(d), q, FAKE, heads(*hs), len(hs) if n_heads is None else n_heads,
+                            last_q, nv, ns, fv, fs, vidx, sidx, vsc, ssc, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=1000), 2), (dict(seq_len=0), 2), (dict(head_dim=96), 2), (dict(heads_kv=3), 2),
+    (dict(heads_q=512, heads_kv=1), 2), (dict(dtype=7), 4), (dict(scale=0.0), 2),
+    (dict(scale=float("nan")), 2), (dict(q_stride=(0, 1024 * 128, 100)), 2), (dict(batch=0), 2),
+])
+def test_bad_descriptor_rejected(kw, status):
+    assert vs_call(desc(**kw)) == status
+    assert mi.lib().mi_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hs=(1, 0)), 7), (dict(hs=(0, 4)), 7), (dict(hs=(0, 0)), 7), (dict(n_heads=0), 7),
+    (dict(last_q=0), 3), (dict(last_q=65), 3), (dict(nv=0), 3), (dict(fv=0), 3), (dict(fv=17), 3),
+    (dict(fs=33), 3), (dict(ws_bytes=16), 5), (dict(ws=None), 5), (dict(vidx=None), 1),
+    (dict(q=None), 1), (dict(q=FAKE + 4), 2), (dict(vsc=FAKE), 1),
+])
+def test_vs_estimate_validation(kw, status):
+    assert vs_call(desc(), **kw) == status
+
+
+def test_workspace_sizes():
+    d = desc()
+    l = mi.lib()
+    vs = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_VS_ESTIMATE, 2, 0)
+    # per-chunk row statistics + row statistics + two score rows per listed head
+    assert vs >= 2 * 2 * 1024 * 4 + 2 * 64 * 8
+    bs = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_BLOCK_ESTIMATE, 2, 0)
+    nb = 1024 // 64
+    assert bs >= (2 * nb * 128 + 2 * nb * 128 + 2 * nb * nb) * 4
+    assert l.mi_workspace_bytes(ctypes.byref(d), mi.OP_SPARSE_PREFILL, 0, 0) == 0
+    assert l.mi_workspace_bytes(ctypes.byref(desc(seq_len=10)), mi.OP_VS_ESTIMATE, 2, 0) == 0
+
+
+def test_block_estimate_validation():
+    l = mi.lib()
+    d = desc()
+    call = lambda top=4, ws_bytes=1 << 30, bidx=FAKE: l.mi_block_estimate(
+        ctypes.byref(d), FAKE, FAKE, heads(0, 2), 2, top, bidx, FAKE, None, FAKE, ws_bytes, None)
+    assert call(top=1) == 3
+    assert call(ws_bytes=8) == 5
+    assert call(bidx=None) == 1
+    long = desc(seq_len=64 * 40000)
+    assert l.mi_block_estimate(ctypes.byref(long), FAKE, FAKE, heads(0), 1, 4, FAKE, FAKE, None, FAKE,
+                               1 << 40, None) == 2
+
+
+def index_struct(bcap=32, ccap=16, cols=True):
+    s = mi.MiIndex()
+    s.block_count, s.block_idx = FAKE, FAKE
+    s.col_count, s.col_idx = FAKE, (FAKE if cols else None)
+    s.block_cap, s.col_cap = bcap, ccap
+    return s
+
+
+def test_build_index_validation():
+    l = mi.lib()
+    d = desc()  # nb = 16
+    pat = lambda *p: ctypes.cast((ctypes.c_int32 * 4)(*p), ctypes.c_void_p)
+
+    def call(p, nv=16, ns=32, top=4, sink=128, local=256, out=None, vidx=FAKE, bs=FAKE):
+        out = out or index_struct()
+        return l.mi_build_index(ctypes.byref(d), p, vidx, nv, FAKE, ns, bs, FAKE, top, sink, local,
+                                ctypes.byref(out), None)
+
+    assert call(pat(0, 1, 2, 9)) == 7
+    assert call(None) == 1
+    assert call(pat(1, 1, 1, 1), vidx=None) == 1
+    assert call(pat(1, 1, 1, 1), out=index_struct(bcap=15)) == 3       # min(nb, 2*32) = 16
+    assert call(pat(1, 1, 1, 1), out=index_struct(ccap=15)) == 3       # min(16, 1024)
+    assert call(pat(1, 1, 1, 1), out=index_struct(cols=False)) == 1
+    assert call(pat(2, 2, 2, 2), top=40, out=index_struct(bcap=15)) == 3  # min(top, nb) = 16
+    assert call(pat(2, 2, 2, 2), bs=None) == 1
+    assert call(pat(0, 0, 0, 0), local=0) == 3
+    assert call(pat(0, 0, 0, 0), sink=64, local=1000, out=index_struct(bcap=10)) == 3  # 1 + 17 -> 16
+    assert call(pat(0, 0, 0, 0), sink=-1) == 3
+
+
+def test_sparse_prefill_validation():
+    l = mi.lib()
+    d = desc()
+    pat = lambda *p: ctypes.cast((ctypes.c_int32 * 4)(*p), ctypes.c_void_p)
+
+    def call(p, idx=None, sink=128, local=256, o=FAKE):
+        return l.mi_sparse_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, p,
+                                   None if idx is None else ctypes.byref(idx), sink, local, o, None,
+                                   None, 0, None)
+
+    assert call(pat(1, 1, 1, 1)) == 1                      # sparse heads need an index
+    assert call(pat(1, 3, 3, 3), index_struct(cols=False)) == 1
+    assert call(pat(0, 3, 3, 3), index_struct(), local=0) == 3
+    assert call(pat(5, 3, 3, 3), index_struct()) == 7
+    assert call(None, o=None) == 1
+    assert call(None, o=FAKE + 8) == 2

@@ -1,0 +1,255 @@
+"""GPU parity of each entry point against the oracle at small sizes that
+still span several tiles, chunks and ragged tails, plus edge cases.
+
+Run on the GPU: every call goes through the C ABI (libmi_sparse.so)."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_amd as mi
+import workloads as W
+from oracle import minference_oracle as O
+from tests.parity_util import (BF16_ATOL, F32_ATOL, assert_scores_close, check_selection, f64,
+                               gpu_index_lists, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mi.lib()
+
+
+def _inputs(seed, hq, hkv, n, d, dtype, batch=1, std=1.0):
+    q, k, v = W.random_qkv(seed, hq, hkv, n, d, dtype, batch=batch, scale_std=std)
+    return (q, k, v), tuple(to_device(x, dtype) for x in (q, k, v)), tuple(W.to_f64(x, dtype) for x in (q, k, v))
+
+
+# ----------------------------------------------------------------- dense
+
+@pytest.mark.parametrize("dtype,d,n,hq,hkv", [("f32", 64, 256, 2, 1), ("bf16", 128, 512, 4, 2),
+                                              ("bf16", 64, 192, 3, 3), ("f32", 128, 128, 2, 2)])
+def test_dense_attention(dtype, d, n, hq, hkv):
+    say(f"dense {dtype} d={d} n={n} hq={hq} hkv={hkv}")
+    _, (q, k, v), (q64, k64, v64) = _inputs(1, hq, hkv, n, d, dtype)
+    o, lse = mi.sparse_prefill(q, k, v, None, None)
+    torch.cuda.synchronize()
+    of, lf = f64(o), f64(lse)
+    g = hq // hkv
+    atol = F32_ATOL if dtype == "f32" else BF16_ATOL
+    for h in range(hq):
+        ref, rlse = O.dense_causal_attention(q64[0, h], k64[0, h // g], v64[0, h // g], d ** -0.5)
+        assert np.abs(of[0, h] - ref).max() < atol, (h, np.abs(of[0, h] - ref).max())
+        assert np.abs(lf[0, h] - rlse).max() < 1e-3
+
+
+def test_dense_attention_strided_batch():
+    """batch 2, inputs given as [B, N, H, d] memory viewed as [B, H, N, d]."""
+    say("dense strided batch")
+    B, hq, hkv, n, d = 2, 4, 2, 256, 128
+    g = np.random.default_rng(3)
+    qn = g.standard_normal((B, n, hq, d)).astype(np.float32)
+    kn = g.standard_normal((B, n, hkv, d)).astype(np.float32)
+    vn = g.standard_normal((B, n, hkv, d)).astype(np.float32)
+    q = torch.from_numpy(qn).cuda().to(torch.bfloat16).transpose(1, 2)
+    k = torch.from_numpy(kn).cuda().to(torch.bfloat16).transpose(1, 2)
+    v = torch.from_numpy(vn).cuda().to(torch.bfloat16).transpose(1, 2)
+    out = torch.empty((B, n, hq, d), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o, _ = mi.sparse_prefill(q, k, v, None, None, out=out)
+    torch.cuda.synchronize()
+    of = f64(o)
+    for b in range(B):
+        for h in range(hq):
+            qq, kk, vv = (f64(t[b, hh]) for t, hh in ((q, h), (k, h // 2), (v, h // 2)))
+            ref, _ = O.dense_causal_attention(qq, kk, vv, d ** -0.5)
+            assert np.abs(of[b, h] - ref).max() < BF16_ATOL
+
+
+# ----------------------------------------------------------------- attention from a given index
+
+def _random_index(rng, nb, n, with_cols=True):
+    lists, cols = [], []
+    for a in range(nb):
+        k = rng.integers(1, a + 2)
+        bl = np.unique(np.concatenate([[a], rng.choice(a + 1, k, replace=True)]))
+        lists.append(bl)
+        if with_cols:
+            cand = np.arange(64 * a + 64)
+            cand = cand[~np.isin(cand // 64, bl)]
+            m = min(len(cand), int(rng.integers(0, 150)))
+            cols.append(np.sort(rng.choice(cand, m, replace=False)) if m else np.zeros(0, np.int64))
+        else:
+            cols.append(np.zeros(0, np.int64))
+    return lists, cols
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_attention_given_index(dtype, d):
+    """Block lists and ragged column lists chosen at random (not by an estimate)."""
+    say(f"attention from a random index {dtype} d={d}")
+    hq, hkv, n = 2, 1, 64 * 11
+    nb = n // 64
+    _, (q, k, v), (q64, k64, v64) = _inputs(5, hq, hkv, n, d, dtype)
+    rng = np.random.default_rng(7)
+    bcap, ccap = nb, 160
+    idx = mi.alloc_index(1, hq, n, bcap, ccap, "cuda")
+    ref_lists = {}
+    bc = np.zeros((1, hq, nb), np.int32)
+    bi = -np.ones((1, hq, nb, bcap), np.int32)
+    cc = np.zeros((1, hq, nb), np.int32)
+    ci = -np.ones((1, hq, nb, ccap), np.int32)
+    for h in range(hq):
+        lists, cols = _random_index(rng, nb, n)
+        for a in range(nb):
+            bc[0, h, a] = len(lists[a]); bi[0, h, a, :len(lists[a])] = lists[a]
+            cc[0, h, a] = len(cols[a]); ci[0, h, a, :len(cols[a])] = cols[a]
+            ref_lists[h, a] = (lists[a], cols[a])
+    for t, src in ((idx.block_count, bc), (idx.block_idx, bi), (idx.col_count, cc), (idx.col_idx, ci)):
+        t.copy_(torch.from_numpy(src))
+    o, lse = mi.sparse_prefill(q, k, v, [W.VSLASH] * hq, idx)
+    torch.cuda.synchronize()
+    of, lf = f64(o), f64(lse)
+    atol = F32_ATOL if dtype == "f32" else BF16_ATOL
+    for h in range(hq):
+        for a in range(nb):
+            blocks, cols = ref_lists[h, a]
+            ref, rlse = O.attention_from_index(q64[0, h], k64[0, 0], v64[0, 0], d ** -0.5, a, blocks, cols)
+            rows = slice(64 * a, 64 * a + 64)
+            assert np.abs(of[0, h, rows] - ref).max() < atol, (h, a)
+            assert np.abs(lf[0, h, rows] - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("sink,local", [(128, 256), (0, 1), (64, 64), (100, 300), (5, 1000)])
+def test_ashape_attention(sink, local):
+    say(f"A-shape sink={sink} local={local}")
+    hq, hkv, n, d = 2, 1, 64 * 13, 128
+    _, (q, k, v), (q64, k64, v64) = _inputs(9, hq, hkv, n, d, "bf16")
+    idx = mi.build_index(q, k, [W.ASHAPE] * hq, sink=sink, local=local)
+    o, _ = mi.sparse_prefill(q, k, v, [W.ASHAPE] * hq, idx, sink=sink, local=local)
+    torch.cuda.synchronize()
+    of = f64(o)
+    for h in range(hq):
+        for a in range(n // 64):
+            blocks, cols = gpu_index_lists(idx, 0, h, a)
+            assert list(blocks) == list(O.ashape_block_list(a, sink, local, n))
+            assert len(cols) == 0
+            rows = np.arange(64 * a, 64 * a + 64)
+            ref, _ = O.ashape_attention(q64[0, h], k64[0, 0], v64[0, 0], d ** -0.5, rows, sink, local)
+            assert np.abs(of[0, h, rows] - ref).max() < BF16_ATOL, (h, a)
+
+
+# ----------------------------------------------------------------- Vertical-Slash estimate
+
+@pytest.mark.parametrize("dtype,d,n,last_q,nv,ns,fv,fs", [
+    ("f32", 64, 2048, 64, 64, 128, 1, 1),
+    ("bf16", 128, 64 * 37, 64, 100, 300, 1, 1),     # ragged: N not a multiple of the chunks
+    ("bf16", 128, 640, 17, 40, 50, 3, 2),           # last_q < 64, wider forced sets
+    ("bf16", 64, 128, 64, 500, 500, 1, 1),          # budgets above N: clamped, -1 padded
+    ("f32", 128, 64, 1, 8, 8, 1, 1),                # single block, single query
+])
+def test_vs_estimate(dtype, d, n, last_q, nv, ns, fv, fs):
+    say(f"vs_estimate {dtype} d={d} n={n} last_q={last_q} nv={nv} ns={ns}")
+    hq, hkv = 4, 2
+    _, (q, k, _), (q64, k64, _) = _inputs(11, hq, hkv, n, d, dtype)
+    heads = [0, 1, 3]
+    vidx, sidx, vsc, ssc = mi.vs_estimate(q, k, heads, last_q, nv, ns, fv, fs)
+    torch.cuda.synchronize()
+    vsc, ssc, vidx, sidx = f64(vsc), f64(ssc), vidx.cpu().numpy(), sidx.cpu().numpy()
+    for h in heads:
+        rv, rs = O.vs_estimate(q64[0, h], k64[0, h // 2], d ** -0.5, last_q)
+        assert_scores_close(vsc[0, h], rv, f"vertical h{h}")
+        assert_scores_close(ssc[0, h], rs, f"slash h{h}")
+        check_selection(vidx[0, h], vsc[0, h], rv, nv, range(fv), f"vertical h{h}")
+        check_selection(sidx[0, h], ssc[0, h], rs, ns, range(fs), f"slash h{h}")
+    assert not vsc[0, 2].any() and not vidx[0, 2].any()  # unlisted head untouched
+
+
+def test_vs_estimate_without_score_outputs_is_identical():
+    say("vs_estimate workspace scores")
+    _, (q, k, _), _ = _inputs(12, 2, 1, 1024, 128, "bf16")
+    a = mi.vs_estimate(q, k, [0, 1], 64, 50, 80)
+    b = mi.vs_estimate(q, k, [0, 1], 64, 50, 80, return_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------- Block-Sparse estimate
+
+@pytest.mark.parametrize("dtype,d,n,top", [("bf16", 128, 64 * 40, 6), ("f32", 64, 64 * 9, 3),
+                                           ("bf16", 128, 64 * 5, 100), ("bf16", 64, 64 * 70, 2)])
+def test_block_estimate(dtype, d, n, top):
+    say(f"block_estimate {dtype} d={d} n={n} top={top}")
+    hq, hkv = 4, 2
+    _, (q, k, _), (q64, k64, _) = _inputs(13, hq, hkv, n, d, dtype)
+    heads = [1, 2]
+    bidx, bcnt, w = mi.block_estimate(q, k, heads, top)
+    torch.cuda.synchronize()
+    bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    nb = n // 64
+    for h in heads:
+        rw, kept = O.bs_estimate(q64[0, h], k64[0, h // 2], d ** -0.5, top)
+        tri = np.tril(np.ones((nb, nb), bool))
+        assert_scores_close(w[0, h][tri], rw[tri], f"block weights h{h}")
+        assert not w[0, h][~tri].any()
+        for a in range(nb):
+            kk = min(top, a + 1)
+            assert bcnt[0, h, a] == kk
+            check_selection(bidx[0, h, a], w[0, h, a, : a + 1], rw[a, : a + 1], kk, {0, a},
+                            f"blocks h{h} a{a}")
+
+
+# ----------------------------------------------------------------- index building
+
+@pytest.mark.parametrize("n,nv,ns", [(64 * 23, 40, 60), (64 * 8, 600, 600), (64 * 40, 5, 1)])
+def test_build_index_vs(n, nv, ns):
+    say(f"build_index VS n={n} nv={nv} ns={ns}")
+    hq, hkv, d = 2, 1, 128
+    _, (q, k, _), _ = _inputs(17, hq, hkv, n, d, "bf16")
+    vidx, sidx, _, _ = mi.vs_estimate(q, k, [0, 1], 64, nv, ns)
+    idx = mi.build_index(q, k, [W.VSLASH] * hq, vidx, sidx)
+    torch.cuda.synchronize()
+    V, S = vidx.cpu().numpy(), sidx.cpu().numpy()
+    for h in range(hq):
+        Vh, Sh = V[0, h][V[0, h] >= 0], S[0, h][S[0, h] >= 0]
+        for a in range(n // 64):
+            blocks, cols = gpu_index_lists(idx, 0, h, a)
+            rb = O.vs_block_list(a, Sh)
+            assert np.array_equal(blocks, rb), (h, a)
+            assert np.array_equal(cols, O.vs_column_list(a, Vh, rb)), (h, a)
+        assert np.all(idx.block_idx[0, h].cpu().numpy()[np.arange(idx.block_cap)[None, :] >=
+                                                        idx.block_count[0, h].cpu().numpy()[:, None]] == -1)
+
+
+def test_build_index_mixed_and_dense_counts():
+    say("build_index mixed")
+    n, hq, hkv, d = 64 * 19, 4, 2, 128
+    _, (q, k, _), _ = _inputs(19, hq, hkv, n, d, "bf16")
+    pat = [W.BSPARSE, W.DENSE, W.ASHAPE, W.BSPARSE]
+    bidx, bcnt, _ = mi.block_estimate(q, k, [0, 3], 5)
+    idx = mi.build_index(q, k, pat, None, None, bidx, bcnt, 5, sink=70, local=200)
+    torch.cuda.synchronize()
+    B = bidx.cpu().numpy()
+    for a in range(n // 64):
+        for h in (0, 3):
+            blocks, cols = gpu_index_lists(idx, 0, h, a)
+            assert np.array_equal(blocks, B[0, h, a, : min(5, a + 1)]) and len(cols) == 0
+        assert int(idx.block_count[0, 1, a]) == a + 1 and int(idx.col_count[0, 1, a]) == 0
+        blocks, _ = gpu_index_lists(idx, 0, 2, a)
+        assert list(blocks) == list(O.ashape_block_list(a, 70, 200, n))
+
+
+def test_index_is_deterministic():
+    say("determinism")
+    n = 64 * 30
+    _, (q, k, _), _ = _inputs(23, 4, 2, n, 128, "bf16")
+    outs = []
+    for _ in range(2):
+        vidx, sidx, vs, ss = mi.vs_estimate(q, k, [0, 1, 2, 3], 64, 70, 90)
+        bidx, bcnt, w = mi.block_estimate(q, k, [0, 1, 2, 3], 7)
+        idx = mi.build_index(q, k, [W.VSLASH] * 4, vidx, sidx)
+        outs.append([vidx, sidx, vs, ss, bidx, bcnt, w, idx.block_idx, idx.col_idx])
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
