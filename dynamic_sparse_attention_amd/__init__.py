@@ -304,3 +304,79 @@ def layer_prefill(q, k, v, head_pattern: Sequence[int], *, last_q=64, n_vertical
                             stream=stream)
     return o, lse, dict(vertical_idx=vidx, slash_idx=sidx, bs_block_idx=bidx, bs_block_count=bcnt,
                         index=index)
+
+
+class LayerPlan:
+    """Buffers for one layer's hot path, allocated once; run() only enqueues
+    the four library calls (estimates, index, attention) on one stream."""
+
+    def __init__(self, q, k, v, head_pattern: Sequence[int], *, last_q=64, n_vertical=1000,
+                 n_slash=6096, force_vertical=1, force_slash=1, top_blocks=100, sink=128,
+                 local=4096, scale=None, with_lse=False):
+        self.q, self.k, self.v = q, k, v
+        self.pat = [int(p) for p in head_pattern]
+        B, Hq, N, d = q.shape
+        dev = q.device
+        self.kw = dict(last_q=last_q, n_vertical=n_vertical, n_slash=n_slash,
+                       force_vertical=force_vertical, force_slash=force_slash,
+                       top_blocks=top_blocks, sink=sink, local=local)
+        self.scale = scale
+        self.vs_heads = [h for h, p in enumerate(self.pat) if p == VSLASH]
+        self.bs_heads = [h for h, p in enumerate(self.pat) if p == BSPARSE]
+        self.desc = make_desc(q, k, scale=scale)
+        self.vidx = self.sidx = self.bidx = self.bcnt = None
+        if self.vs_heads:
+            self.vidx = torch.zeros((B, Hq, n_vertical), dtype=torch.int32, device=dev)
+            self.sidx = torch.zeros((B, Hq, n_slash), dtype=torch.int32, device=dev)
+            self.vs_ws = _workspace(workspace_bytes(self.desc, OP_VS_ESTIMATE, len(self.vs_heads)), dev)
+            self.vs_heads_c = _heads_arr(self.vs_heads)
+        if self.bs_heads:
+            nb = N // MI_BLOCK
+            self.bidx = torch.zeros((B, Hq, nb, top_blocks), dtype=torch.int32, device=dev)
+            self.bcnt = torch.zeros((B, Hq, nb), dtype=torch.int32, device=dev)
+            self.bs_ws = _workspace(workspace_bytes(self.desc, OP_BLOCK_ESTIMATE, len(self.bs_heads)), dev)
+            self.bs_heads_c = _heads_arr(self.bs_heads)
+        bcap, ccap = index_caps(N, self.pat, n_vertical, n_slash, top_blocks, sink, local)
+        self.index = alloc_index(B, Hq, N, bcap, ccap, dev)
+        self.index_c = self.index.c_struct()
+        self.pat_c = (ctypes.c_int32 * Hq)(*self.pat)
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
+        self.attn_desc = make_desc(q, k, v, self.o, scale=scale)
+
+    def estimate(self, stream=None):
+        kw, s, l = self.kw, _stream(stream), lib()
+        if self.vs_heads:
+            _check(l.mi_vs_estimate(ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k),
+                                    ctypes.cast(self.vs_heads_c, _P), len(self.vs_heads), kw["last_q"],
+                                    kw["n_vertical"], kw["n_slash"], kw["force_vertical"],
+                                    kw["force_slash"], _ptr(self.vidx), _ptr(self.sidx), None, None,
+                                    _ptr(self.vs_ws), self.vs_ws.numel(), s))
+        if self.bs_heads:
+            _check(l.mi_block_estimate(ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k),
+                                       ctypes.cast(self.bs_heads_c, _P), len(self.bs_heads),
+                                       kw["top_blocks"], _ptr(self.bidx), _ptr(self.bcnt), None,
+                                       _ptr(self.bs_ws), self.bs_ws.numel(), s))
+
+    def build_index(self, stream=None):
+        kw = self.kw
+        nv = kw["n_vertical"] if self.vs_heads else 0
+        ns = kw["n_slash"] if self.vs_heads else 0
+        _check(lib().mi_build_index(ctypes.byref(self.desc), ctypes.cast(self.pat_c, _P), _ptr(self.vidx),
+                                    nv, _ptr(self.sidx), ns, _ptr(self.bidx), _ptr(self.bcnt),
+                                    kw["top_blocks"], kw["sink"], kw["local"], ctypes.byref(self.index_c),
+                                    _stream(stream)))
+
+    def attention(self, stream=None, dense=False):
+        kw = self.kw
+        _check(lib().mi_sparse_prefill(ctypes.byref(self.attn_desc), _ptr(self.q), _ptr(self.k),
+                                       _ptr(self.v), None if dense else ctypes.cast(self.pat_c, _P),
+                                       None if dense else ctypes.byref(self.index_c), kw["sink"],
+                                       kw["local"], _ptr(self.o), _ptr(self.lse), None, 0,
+                                       _stream(stream)))
+
+    def run(self, stream=None):
+        self.estimate(stream)
+        self.build_index(stream)
+        self.attention(stream)
+        return self.o
