@@ -22,6 +22,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the softmax
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
