@@ -42,7 +42,39 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", action="store_true", help="also time the dense causal comparator once")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A copy of known size: 4 launches, each reading and writing 1 GiB, so
+    that HBM byte counters can be scaled against known traffic."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": {"launches": 4, "bytes_read_per_launch": 1 << 30,
+                                         "bytes_written_per_launch": 1 << 30}}))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload with the current kernel source;
+    otherwise None (the counters describe another kernel)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "sparse_attn_vs128k_hbm.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("sparse_attn.hip", "mi_device.h"))
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def index_work(plan, d):
@@ -128,6 +160,9 @@ def cpu_baseline(w, data, plan, budget_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding by kv-head "
                           "group is designed but not built", "n_gpus": args.gpus}))
@@ -205,7 +240,8 @@ def main():
                    "last_q": w.last_q, "n_vertical": w.n_vertical, "n_slash": w.n_slash,
                    "top_blocks": w.top_blocks, "sink": w.sink, "local": w.local},
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name),
                      "flop_per_launch": flop},
         "kernels_ms": {"estimate": round(est_ms, 4), "build_index": round(idx_ms, 4),
                        "attention": round(att_ms, 4)},
