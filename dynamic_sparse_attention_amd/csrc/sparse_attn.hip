@@ -25,11 +25,12 @@
 // consecutive LDS per instruction) into two buffers: the loads of step t+1
 // are in flight while step t is computed, with one barrier per step.  Rows
 // are stored unpadded; 16-byte chunk c of row r sits at position c ^ f(r),
-// f(r) = 2(r%4) + (r/4)%2, so that the K operand reads (8 consecutive rows,
-// same chunk) and the V transposed reads (4 rows, 2 chunks) hit distinct
-// LDS banks.  bf16: the V^T operand is read with the gfx950 LDS transpose
-// read (ds_read_b64_tr_b16), which hands lane i of a 16-lane group element
-// (i%4) of the 8-byte rows addressed by lanes 4j + i/4, j = 0..3.  fp32: V^T
+// f(r) = 4(r%4) + (r/4)%4 (16-chunk rows), so that a K operand read (16 lanes
+// per LDS cycle: 16 consecutive rows, same chunk) and a V transposed read
+// (32 lanes per cycle: 4 rows x 4 chunks) each hit all 64 banks once.
+// bf16: the V^T operand is read with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16), which hands lane i of a 16-lane group element (i%4)
+// of the 8-byte rows addressed by lanes 4j + i/4, j = 0..3.  fp32: V^T
 // elements are read one by one.
 #include "mi_device.h"
 #include "mi_internal.h"
@@ -83,7 +84,13 @@ struct Buf {
     int32_t colpos[64];
 };
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Chunk swizzle of a staged row (see the header comment); rows of 8 chunks
+// (bf16, d = 64) use 4((r/2)%2) + (r/4)%4.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (CPR == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+}
 
 // One step of the item: a merged key tile or a chunk of one block's columns.
 struct Step {
@@ -93,6 +100,14 @@ struct Step {
     int blk;    // column chunk: owning block (0 / 1)
     int c0;     // column chunk: first list position
 };
+
+// Wave-uniform read of an index list entry through the constant address
+// space, which the backend issues as a scalar (s_load) read: the lists are
+// not written while the kernel runs.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int ld_uniform(const int32_t* p) {
+    return *reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(p));
+}
 
 struct Walker {
     int dense, a0, a1, has1;
@@ -115,12 +130,15 @@ struct Walker {
                 return s;
             }
         } else {
-            // ascending merge of the two lists; entries outside [0, a] are skipped
-            while (p0 < n0 && (unsigned)L0[p0] > (unsigned)a0) ++p0;
-            while (p1 < n1 && (unsigned)L1[p1] > (unsigned)a1) ++p1;
+            // ascending merge of the two lists; entries outside [0, a] are
+            // skipped.  All walker state is wave-uniform: readfirstlane keeps
+            // the list reads on the scalar unit (scalar cache) instead of
+            // per-lane memory loads with a full wait each.
+            while (p0 < n0 && (unsigned)ld_uniform(L0 + p0) > (unsigned)a0) ++p0;
+            while (p1 < n1 && (unsigned)ld_uniform(L1 + p1) > (unsigned)a1) ++p1;
             if (p0 < n0 || p1 < n1) {
-                const int k0 = p0 < n0 ? L0[p0] : 0x7FFFFFFF;
-                const int k1 = p1 < n1 ? L1[p1] : 0x7FFFFFFF;
+                const int k0 = p0 < n0 ? ld_uniform(L0 + p0) : 0x7FFFFFFF;
+                const int k1 = p1 < n1 ? ld_uniform(L1 + p1) : 0x7FFFFFFF;
                 const int kb = k0 < k1 ? k0 : k1;
                 s.kind = 0;
                 s.kb = kb;
@@ -161,7 +179,7 @@ __device__ __forceinline__ void issue_step(Buf<T, D>& buf, const Step& s, const 
         const int idx = it * kWaves + wave;
         const int cidx = idx * 64 + lane;
         const int row = cidx / Ly::CPR, pos = cidx % Ly::CPR;
-        const int chunk = pos ^ swz(row);
+        const int chunk = pos ^ swz<Ly::CPR>(row);
         int tok;
         if (s.kind == 0) {
             tok = s.kb * 64 + row;
@@ -190,31 +208,36 @@ template <typename T, int D>
 struct LaneOffsets {
     int krow;          // row part of the K operand address: (kh*32 + rl) handled by + kh*32*ROWB
     int kpos[D / 16];  // chunk part for contraction step ks
-    int vrow;          // V operand: row part (keys base + 4hl + j)
-    int vpos[D / 32];  // chunk part for d block db
+    int vrow;              // V operand: row part (keys base + 4hl + j)
+    int vpos[D / 32][2];   // chunk part for d block db, rows +0 / +8
 };
 
 template <typename T, int D>
 __device__ __forceinline__ void lane_offsets(LaneOffsets<T, D>& o, int lane) {
     typedef Layout<T, D> Ly;
     const int rl = lane & 31, hl = lane >> 5;
-    const int f = swz(rl);
+    // row kh*32 + rl has the swizzle of rl (kh*32 leaves the low 4 bits alone)
+    const int f = swz<Ly::CPR>(rl);
     o.krow = rl * Ly::ROWB;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) o.kpos[ks] = ((2 * ks + hl) ^ f) * 16;
         const int g16 = (lane >> 4) & 1, s = lane & 15, j = s >> 2, qd = s & 3;
         o.vrow = (4 * hl + j) * Ly::ROWB;
-        const int fv = swz(4 * hl + j);
+        // rows base + 4hl + j and base + 8 + 4hl + j, base a multiple of 16
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            o.vpos[db] = ((4 * db + 2 * g16 + (qd >> 1)) ^ fv) * 16 + (qd & 1) * 8;
+        for (int sec = 0; sec < 2; ++sec) {
+            const int fv = swz<Ly::CPR>(8 * sec + 4 * hl + j);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                o.vpos[db][sec] = ((4 * db + 2 * g16 + (qd >> 1)) ^ fv) * 16 + (qd & 1) * 8;
+        }
     } else {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) o.kpos[ks] = ((4 * ks + 2 * hl) ^ f) * 16;
         o.vrow = 0;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o.vpos[db] = 0;
+        for (int db = 0; db < D / 32; ++db) o.vpos[db][0] = o.vpos[db][1] = 0;
     }
 }
 
@@ -228,7 +251,7 @@ template <int D>
 __device__ __forceinline__ f32x8 k_frag(const char* kb, const LaneOffsets<float, D>& o, int kh, int ks) {
     const int rl = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
     const char* row = kb + kh * 32 * Layout<float, D>::ROWB + o.krow;
-    const int f = swz(rl);
+    const int f = swz<Layout<float, D>::CPR>(rl);
     const f32x4 a = *reinterpret_cast<const f32x4*>(row + o.kpos[ks]);
     const f32x4 b = *reinterpret_cast<const f32x4*>(row + (((4 * ks + 2 * hl + 1) ^ f) * 16));
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -239,8 +262,8 @@ __device__ __forceinline__ f32x8 k_frag(const char* kb, const LaneOffsets<float,
 template <int D>
 __device__ __forceinline__ bf16x8 v_frag(const char* vb, const LaneOffsets<uint16_t, D>& o, int db, int base) {
     constexpr int RB = Layout<uint16_t, D>::ROWB;
-    const char* p0 = vb + base * RB + o.vrow + o.vpos[db];
-    const char* p1 = p0 + 8 * RB;
+    const char* p0 = vb + base * RB + o.vrow + o.vpos[db][0];
+    const char* p1 = vb + (base + 8) * RB + o.vrow + o.vpos[db][1];
     const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
     const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
     const i16x8 r = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -255,7 +278,8 @@ __device__ __forceinline__ f32x8 v_frag(const char* vb, const LaneOffsets<float,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int key = base + (e >> 2) * 8 + 4 * hl + (e & 3);
-        r[e] = *reinterpret_cast<const float*>(vb + key * RB + (((d >> 2) ^ swz(key)) * 16) + (d & 3) * 4);
+        r[e] = *reinterpret_cast<const float*>(vb + key * RB + (((d >> 2) ^ swz<Layout<float, D>::CPR>(key)) * 16) +
+                                               (d & 3) * 4);
     }
     return r;
 }
