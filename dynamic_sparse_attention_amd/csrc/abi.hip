@@ -296,6 +296,13 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
     a.sink = sink_tokens; a.local = local_tokens;
     a.all_dense = head_pattern ? 0 : 1;
     for (int h = 0; h < d->heads_q; ++h) a.pattern[h] = head_pattern ? (uint8_t)head_pattern[h] : (uint8_t)MI_DENSE;
+    const size_t es = d->dtype == MI_BF16 ? 2 : 4;
+    if ((uint64_t)d->k_stride[2] * es * MI_BLOCK >= (1ull << 31) || (uint64_t)d->v_stride[2] * es * MI_BLOCK >= (1ull << 31))
+        return fail(MI_ERR_SHAPE, "K/V token strides too large (64 rows must span < 2 GiB)");
+    const size_t lds = mi::sparse_attn_lds_bytes(a);
+    if (lds > mi::kAttnMaxLds)
+        return fail(MI_ERR_SHAPE, "attention needs %zu bytes of LDS (> %zu): seq_len or col_cap too large", lds,
+                    mi::kAttnMaxLds);
     return launched(mi::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -28,6 +28,12 @@ struct AttnArgs {
     uint8_t pattern[MI_MAX_HEADS];
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// LDS of one attention workgroup: four K/V staging tiles, the four column
+// lists of a run of query blocks and its step list (grows with seq_len and
+// col_cap).
+constexpr size_t kAttnMaxLds = 160 * 1024;
+int attn_col_stride(const AttnArgs& a);
+size_t sparse_attn_lds_bytes(const AttnArgs& a);
 
 struct VsArgs {
     const void* q;

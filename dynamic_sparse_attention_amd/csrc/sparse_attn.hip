@@ -1,18 +1,20 @@
 // Block + column sparse flash attention for gfx950 (and its dense-causal
-// comparator).
+// comparator).  An online softmax keeps a running max and normaliser per row
+// in fp32 (aifetchly guide, "1. The Vertical-Slash Kernel Mechanics"); tiles
+// that no index list names are never touched ("2. The Block-Sparse Kernel
+// Mechanics").
 //
-// Work item: one (batch, query head, pair of 64-row query blocks a0 = 2p,
-// a1 = 2p+1).  The two blocks share every staged K/V tile: the item walks the
-// ascending merge of their key-block lists; a tile listed by only one block
-// is computed only by that block's wavefronts.  Then each block's gathered
-// column list is walked in chunks of 64 keys.  An online softmax keeps a
-// running max and normaliser per row in fp32 (aifetchly guide, "1. The
-// Vertical-Slash Kernel Mechanics"); tiles not listed are never touched
-// ("2. The Block-Sparse Kernel Mechanics").
+// Work item: one (batch, query head, run of four 64-row query blocks
+// a_i = 4r + i).  The four blocks share every staged K/V tile.  At the start
+// of an item the workgroup writes the item's step list to LDS: the ascending
+// merge of the four key-block lists, each entry carrying a 4-bit mask of the
+// blocks that list it, followed by the column chunks (64 gathered keys) of
+// blocks a_0..a_3; the four column lists themselves are copied to LDS too.
 //
-// Workgroup: 4 wavefronts; wavefront w owns rows [32(w%2), 32(w%2)+32) of
-// block a_{w/2}.  Both MFMA stages are computed transposed so that one lane
-// owns one query row from the scores to the output:
+// Workgroup: 8 wavefronts in two groups of four (one wavefront of each group
+// per SIMD).  Group g owns blocks a_{2g}, a_{2g+1}; each wavefront owns 32
+// rows.  Both MFMA stages are computed transposed so that one lane owns one
+// query row from the scores to the output:
 //     S^T (64 keys x 32 rows)  = K_tile (64 x D) . Q^T (D x 32)
 //     O^T (D x 32 rows)       += V^T (D x 64)    . P^T (64 x 32)
 // With the 32x32 MFMA result layout, lane l holds query row l%32 and 16 of
@@ -20,17 +22,25 @@
 // product without any cross-lane move, and each row's statistics live on the
 // lane pair (l, l^32).
 //
+// Ping-pong schedule.  A wavefront's work on step t is split into an MFMA
+// phase M(t) = {P.V of step t-1, S of step t, its mask and row max} and a
+// vector phase V(t) = {running-max update, exponentials, P}.  Phases are
+// separated by workgroup barriers; group 0 runs M(t) while group 1 runs
+// V(t-1), then group 0 runs V(t) while group 1 runs M(t), so the two
+// wavefronts sharing a SIMD keep the matrix cores and the vector ALUs busy
+// at the same time.
+//
 // Staging: K and V rows go from global memory straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane, a wave writes 1 KiB of
-// consecutive LDS per instruction) into two buffers: the loads of step t+1
-// are in flight while step t is computed, with one barrier per step.  Rows
-// are stored unpadded; 16-byte chunk c of row r sits at position c ^ f(r),
-// f(r) = 4(r%4) + (r/4)%4 (16-chunk rows), so that a K operand read (16 lanes
-// per LDS cycle: 16 consecutive rows, same chunk) and a V transposed read
-// (32 lanes per cycle: 4 rows x 4 chunks) each hit all 64 banks once.
-// bf16: the V^T operand is read with the gfx950 LDS transpose read
-// (ds_read_b64_tr_b16), which hands lane i of a 16-lane group element (i%4)
-// of the 8-byte rows addressed by lanes 4j + i/4, j = 0..3.  fp32: V^T
+// (global_load_lds_dwordx4, 16 bytes per lane, 1 KiB of consecutive LDS per
+// wave instruction).  K and V each have two buffers; at the start of phase 2t
+// the copies of K(t+1) and V(t) are issued, and they are waited for at the
+// end of phase 2t+1.  Rows are stored unpadded; 16-byte chunk c of row r sits
+// at position c ^ f(r), f(r) = 4(r%4) + (r/4)%4 (16-chunk rows), so that a K
+// operand read (16 lanes per LDS cycle: 16 consecutive rows, same chunk) and
+// a V transposed read (32 lanes per cycle: 4 rows x 4 chunks) each hit all 64
+// banks once.  bf16: the V^T operand is read with the gfx950 LDS transpose
+// read (ds_read_b64_tr_b16), which hands lane i of a 16-lane group element
+// (i%4) of the 8-byte rows addressed by lanes 4j + i/4, j = 0..3.  fp32: V^T
 // elements are read one by one.
 #include "mi_device.h"
 #include "mi_internal.h"
@@ -47,21 +57,23 @@ struct Params {
     char* o;
     float* lse;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;  // element strides
-    int32_t B, Hq, Hkv, N, nb, npairs, group;
+    int32_t B, Hq, Hkv, N, nb, nruns, group;
     float c;  // scale * log2(e)
     const int32_t* block_count;
     const int32_t* block_idx;
     const int32_t* col_count;
     const int32_t* col_idx;
     int32_t block_cap, col_cap;
+    int32_t cstride;  // LDS entries per block column list (col_cap rounded up to 64; 0 without VS heads)
     int32_t sink, local;
     int32_t all_dense;
     int32_t xcd_chunk;
     uint8_t pattern[MI_MAX_HEADS];
 };
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;  // 8 wavefronts, two groups of 4
+constexpr int kBlocks = 4;             // query blocks per work item
 // The running max is only raised when a row's new max exceeds it by more
 // than this (log2 units); probabilities then stay below 2^kLazy, and the
 // result is unchanged because numerator and normaliser share the same max.
@@ -76,30 +88,44 @@ struct Layout {
     static constexpr int TILEB = 64 * ROWB;
 };
 
-// One LDS staging buffer: a 64-key tile (or column chunk) of K and V.
+// LDS of a work item.  Static: four staging tiles of TILEB bytes, K buffers
+// 0/1 and V buffers 0/1 (step t uses buffer t % 2), and the key positions of
+// a column step's 64 slots per K buffer; separate objects, so that the
+// compiler can tell an operand read from the copies still in flight into the
+// other buffers.  Dynamic LDS (byte offsets):
+//   [0, 16 cstride)   column lists of the four blocks (-1 past the end)
+//   then the packed step list (nb + 4 cstride / 64 entries), then 8 scan
+//   slots.  While the step list is built, its first nb bytes hold the
+//   per-key-block need masks.
 template <typename T, int D>
-struct Buf {
-    char k[Layout<T, D>::TILEB];
-    char v[Layout<T, D>::TILEB];
-    int32_t colpos[64];
+struct Arena {
+    static constexpr int kTile = Layout<T, D>::TILEB;
+    static constexpr int kStatic = 4 * kTile + 2 * 64 * 4;  // + the two column-slot position arrays
+    __host__ __device__ static int steps(int cstride) { return 16 * cstride; }
+    __host__ __device__ static int scan(int nb, int cstride) { return steps(cstride) + 4 * (nb + 4 * (cstride / 64)); }
+    __host__ __device__ static int bytes(int nb, int cstride) { return scan(nb, cstride) + 4 * kWaves; }
 };
 
+// Packed step: bits 0-19 key block (tile) or first list position (column
+// chunk), 20-23 mask of the blocks that compute it, 24-25 owning block of a
+// column chunk, 26 column chunk.
+constexpr uint32_t kNoStep = 0xffffffffu;
+__device__ __forceinline__ uint32_t pack_step(int kb, int need, int blk, int col) {
+    return (uint32_t)kb | ((uint32_t)need << 20) | ((uint32_t)blk << 24) | ((uint32_t)col << 26);
+}
+__device__ __forceinline__ int step_kb(uint32_t w) { return (int)(w & 0xfffffu); }
+__device__ __forceinline__ int step_need(uint32_t w) { return (int)((w >> 20) & 15u); }
+__device__ __forceinline__ int step_blk(uint32_t w) { return (int)((w >> 24) & 3u); }
+__device__ __forceinline__ bool step_col(uint32_t w) { return (w >> 26) & 1u; }
+
 // Chunk swizzle of a staged row (see the header comment); rows of 8 chunks
-// (bf16, d = 64) use 4((r/2)%2) + (r/4)%4.
+// (bf16, d = 64) use 4((r/2)%2) + (r/4)%4.  Rows of 32 chunks (fp32,
+// d = 128) use the 16-chunk form, which permutes their positions too.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (CPR == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
     return ((row & 3) << 2) | ((row >> 2) & 3);
 }
-
-// One step of the item: a merged key tile or a chunk of one block's columns.
-struct Step {
-    int kind;   // 0 tile, 1 column chunk, -1 none
-    int kb;     // tile: key block
-    int need;   // bit 0: block a0 computes, bit 1: block a1 computes
-    int blk;    // column chunk: owning block (0 / 1)
-    int c0;     // column chunk: first list position
-};
 
 // Wave-uniform read of an index list entry through the constant address
 // space, which the backend issues as a scalar (s_load) read: the lists are
@@ -109,179 +135,222 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p) {
     return *reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(p));
 }
 
-struct Walker {
-    int dense, a0, a1, has1;
-    const int32_t* L0;
-    const int32_t* L1;
-    int n0, n1, p0, p1, dk;
-    const int32_t* C0;
-    const int32_t* C1;
-    int m0, m1, cpos, cblk;
-
-    __device__ __forceinline__ Step next() {
-        Step s{-1, 0, 0, 0, 0};
-        if (dense) {
-            const int lim = has1 ? a1 : a0;
-            if (dk <= lim) {
-                s.kind = 0;
-                s.kb = dk;
-                s.need = (dk <= a0 ? 1 : 0) | (has1 ? 2 : 0);
-                ++dk;
-                return s;
-            }
-        } else {
-            // ascending merge of the two lists; entries outside [0, a] are
-            // skipped.  All walker state is wave-uniform: readfirstlane keeps
-            // the list reads on the scalar unit (scalar cache) instead of
-            // per-lane memory loads with a full wait each.
-            while (p0 < n0 && (unsigned)ld_uniform(L0 + p0) > (unsigned)a0) ++p0;
-            while (p1 < n1 && (unsigned)ld_uniform(L1 + p1) > (unsigned)a1) ++p1;
-            if (p0 < n0 || p1 < n1) {
-                const int k0 = p0 < n0 ? ld_uniform(L0 + p0) : 0x7FFFFFFF;
-                const int k1 = p1 < n1 ? ld_uniform(L1 + p1) : 0x7FFFFFFF;
-                const int kb = k0 < k1 ? k0 : k1;
-                s.kind = 0;
-                s.kb = kb;
-                s.need = (k0 == kb ? 1 : 0) | (k1 == kb ? 2 : 0);
-                if (k0 == kb) ++p0;
-                if (k1 == kb) ++p1;
-                return s;
-            }
-        }
-        // column chunks of block a0, then of block a1
-        if (cblk == 0 && cpos >= m0) { cblk = 1; cpos = 0; }
-        if (cblk == 0) {
-            s.kind = 1; s.blk = 0; s.c0 = cpos; s.need = 1; cpos += 64;
-            return s;
-        }
-        if (cblk == 1 && cpos < m1) {
-            s.kind = 1; s.blk = 1; s.c0 = cpos; s.need = 2; cpos += 64;
-            return s;
-        }
-        return s;
-    }
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issues the global->LDS copies of one step into `buf`.  Wave-instruction
-// `idx` fills LDS chunks [64 idx, 64 idx + 64) of a tensor: lane l writes
-// chunk 64 idx + l, i.e. row (64 idx + l) / CPR at position (64 idx + l) % CPR,
-// which holds source chunk position ^ f(row).
+// Issues the global->LDS copies of one step's K (or V) rows into the LDS
+// buffer `dst`.  Wave instruction `idx` fills LDS chunks [64 idx, 64 idx + 64):
+// lane l writes chunk 64 idx + l, i.e. row (64 idx + l) / CPR at position
+// (64 idx + l) % CPR, which holds source chunk position ^ f(row).  Tile rows
+// are addressed from a uniform base plus a 32-bit lane offset.  Gathered rows
+// read their key position from `tok_src` (-1: empty slot, which reads row 0
+// and is masked out later); the K copy also records the positions in
+// `tok_dst` for the mask and the V copy of the same step.
 template <typename T, int D>
-__device__ __forceinline__ void issue_step(Buf<T, D>& buf, const Step& s, const Walker& w,
-                                           const T* kbase, const T* vbase, int64_t kstride,
-                                           int64_t vstride, int N) {
+__device__ __forceinline__ void issue_rows(char* dst, uint32_t w, const int32_t* tok_src, int32_t* tok_dst,
+                                           const char* base, int64_t stride_b) {
     typedef Layout<T, D> Ly;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool col = step_col(w);
+    const char* tile = base + (int64_t)step_kb(w) * 64 * stride_b;
 #pragma unroll
     for (int it = 0; it < Ly::CPR / kWaves; ++it) {
         const int idx = it * kWaves + wave;
         const int cidx = idx * 64 + lane;
         const int row = cidx / Ly::CPR, pos = cidx % Ly::CPR;
         const int chunk = pos ^ swz<Ly::CPR>(row);
-        int tok;
-        if (s.kind == 0) {
-            tok = s.kb * 64 + row;
+        const char* src;
+        if (!col) {
+            src = tile + (uint32_t)(row * (int32_t)stride_b + chunk * 16);
         } else {
-            const int li = s.c0 + row;
-            const int32_t* C = s.blk == 0 ? w.C0 : w.C1;
-            const int m = s.blk == 0 ? w.m0 : w.m1;
-            tok = li < m ? C[li] : -1;
-            if (tok >= N) tok = -1;
-            if (pos == 0) buf.colpos[row] = tok;
-            if (tok < 0) tok = 0;  // any valid row: the column is masked out
+            const int tok = tok_src[row];
+            if (tok_dst && pos == 0) tok_dst[row] = tok;
+            src = base + (int64_t)max(tok, 0) * stride_b + chunk * 16;
         }
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)tok * kstride + chunk * Ly::EPC,
-                                         (lds_void*)(buf.k + idx * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + (int64_t)tok * vstride + chunk * Ly::EPC,
-                                         (lds_void*)(buf.v + idx * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + idx * 1024), 16, 0, 0);
     }
+}
+
+// Writes the item's step list (and, for Vertical-Slash heads, the four
+// column lists) to LDS; returns the number of steps.  Sparse heads: a mask
+// byte per key block kb <= a_3 (bit i: block a_i lists kb, kb <= a_i), then
+// an ordered compaction of the non-empty masks.  Dense heads: every causal
+// key block, computed by the blocks at or after it.
+template <typename T, int D>
+__device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, int a0, int nblk) {
+    typedef Arena<T, D> A;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int cstride = p.cstride;
+    uint32_t* steps = reinterpret_cast<uint32_t*>(dyn + A::steps(cstride));
+    int32_t* scan = reinterpret_cast<int32_t*>(dyn + A::scan(p.nb, cstride));
+    const int nkb = a0 + nblk;
+    int ntiles;
+    if (pattern == MI_DENSE) {
+        for (int kb = t; kb < nkb; kb += kThreads) {
+            int need = 0;
+            for (int w = 0; w < nblk; ++w) need |= (kb <= a0 + w) ? (1 << w) : 0;
+            steps[kb] = pack_step(kb, need, 0, 0);
+        }
+        ntiles = nkb;
+    } else {
+        uint32_t* mw = steps;  // nkb mask bytes, packed four per word
+        const int words = (nkb + 3) / 4;
+        for (int i = t; i < words; i += kThreads) mw[i] = 0u;
+        __syncthreads();
+        for (int w = 0; w < nblk; ++w) {
+            const int cnt = min(max(ld_uniform(p.block_count + r0 + w), 0), p.block_cap);
+            const int32_t* L = p.block_idx + (r0 + w) * p.block_cap;
+            for (int i = t; i < cnt; i += kThreads) {
+                const int kb = L[i];
+                if (kb >= 0 && kb <= a0 + w) atomicOr(&mw[kb >> 2], (1u << w) << (8 * (kb & 3)));
+            }
+        }
+        __syncthreads();
+        // thread t owns mask words [t per, (t + 1) per): read them, count the
+        // non-empty masks, scan the counts, then overwrite the region with
+        // the steps (entry o <= key block, so only after every read)
+        constexpr int kMaxPer = 16;  // words per thread: nkb <= 4 * 16 * 512
+        const int per = (words + kThreads - 1) / kThreads;
+        uint32_t mine[kMaxPer];
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int wi = t * per + j;
+            mine[j] = (j < per && wi < words) ? mw[wi] : 0u;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) c += ((mine[j] >> (8 * bb)) & 0xffu) ? 1 : 0;
+        }
+        int incl = c;  // inclusive scan over the wavefront
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) scan[wv] = incl;
+        __syncthreads();
+        int before = 0;
+        ntiles = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            before += w < wv ? scan[w] : 0;
+            ntiles += scan[w];
+        }
+        int o = before + incl - c;
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint32_t m = (mine[j] >> (8 * bb)) & 0xffu;
+                if (m) steps[o++] = pack_step(4 * (t * per + j) + bb, (int)m, 0, 0);
+            }
+    }
+    int nsteps = ntiles;
+    if (pattern == MI_VSLASH) {
+        int32_t* colsl = reinterpret_cast<int32_t*>(dyn);
+        for (int w = 0; w < kBlocks; ++w) {
+            const int cnt = w < nblk ? min(max(ld_uniform(p.col_count + r0 + w), 0), p.col_cap) : 0;
+            const int32_t* C = p.col_idx + (r0 + w) * p.col_cap;
+            for (int i = t; i < cstride; i += kThreads) {
+                const int j = i < cnt ? C[i] : -1;
+                colsl[w * cstride + i] = (j >= 0 && j < p.N) ? j : -1;
+            }
+            const int nch = (cnt + 63) / 64;
+            for (int c = t; c < nch; c += kThreads) steps[nsteps + c] = pack_step(64 * c, 1 << w, w, 1);
+            nsteps += nch;
+        }
+    }
+    __syncthreads();
+    return nsteps;
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Per-lane LDS byte offsets that do not depend on the step.
-template <typename T, int D>
-struct LaneOffsets {
-    int krow;          // row part of the K operand address: (kh*32 + rl) handled by + kh*32*ROWB
-    int kpos[D / 16];  // chunk part for contraction step ks
-    int vrow;              // V operand: row part (keys base + 4hl + j)
-    int vpos[D / 32][2];   // chunk part for d block db, rows +0 / +8
+// Per-lane LDS byte offsets of the operand reads (bf16), relative to a
+// buffer.  With unpadded rows of ROWB >= 128 bytes and the XOR swizzle:
+//   K operand (row kh*32 + rl, chunk 2ks + hl):
+//       rl*ROWB + 16((2ks + hl) ^ f(rl)) = (kbase ^ 32ks),  kbase = rl*ROWB + 16(hl ^ f(rl));
+//   V^T operand (row base + 8sec + 4hl + j, chunk 4db + x, half qd%2), with
+//   x = 2((l/16)%2) + (qd/2) and f(r + 8) = f(r) ^ 2:
+//       (base + 8sec)*ROWB + (vbase ^ (64db + 32sec)),
+//       vbase = (4hl + j)*ROWB + 16(x ^ f(4hl + j)) + 8(qd%2).
+// The XOR constants only touch bits 5..7 (below ROWB); the buffers are
+// 1 KiB aligned.
+struct LaneBase {
+    int k, v;
 };
-
 template <typename T, int D>
-__device__ __forceinline__ void lane_offsets(LaneOffsets<T, D>& o, int lane) {
+__device__ __forceinline__ LaneBase lane_base(int lane) {
     typedef Layout<T, D> Ly;
     const int rl = lane & 31, hl = lane >> 5;
-    // row kh*32 + rl has the swizzle of rl (kh*32 leaves the low 4 bits alone)
-    const int f = swz<Ly::CPR>(rl);
-    o.krow = rl * Ly::ROWB;
+    LaneBase b;
     if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) o.kpos[ks] = ((2 * ks + hl) ^ f) * 16;
+        b.k = rl * Ly::ROWB + 16 * (hl ^ swz<Ly::CPR>(rl));
         const int g16 = (lane >> 4) & 1, s = lane & 15, j = s >> 2, qd = s & 3;
-        o.vrow = (4 * hl + j) * Ly::ROWB;
-        // rows base + 4hl + j and base + 8 + 4hl + j, base a multiple of 16
-#pragma unroll
-        for (int sec = 0; sec < 2; ++sec) {
-            const int fv = swz<Ly::CPR>(8 * sec + 4 * hl + j);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                o.vpos[db][sec] = ((4 * db + 2 * g16 + (qd >> 1)) ^ fv) * 16 + (qd & 1) * 8;
-        }
+        const int x = 2 * g16 + (qd >> 1);
+        b.v = (4 * hl + j) * Ly::ROWB + 16 * (x ^ swz<Ly::CPR>(4 * hl + j)) + 8 * (qd & 1);
     } else {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) o.kpos[ks] = ((4 * ks + 2 * hl) ^ f) * 16;
-        o.vrow = 0;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o.vpos[db][0] = o.vpos[db][1] = 0;
+        b.k = rl * Ly::ROWB;
+        b.v = 0;
     }
+    return b;
 }
 
-// K operand (8 elements of key row kh*32 + rl, slots 16 ks + 8 hl ..).
+// K operand (8 elements of key row kh*32 + rl, slots 16 ks + 8 hl ..) from
+// the K buffer `kbuf`.
 template <int D>
-__device__ __forceinline__ bf16x8 k_frag(const char* kb, const LaneOffsets<uint16_t, D>& o, int kh, int ks) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                          kb + kh * 32 * Layout<uint16_t, D>::ROWB + o.krow + o.kpos[ks]));
+__device__ __forceinline__ bf16x8 k_frag_bf16(const char* kbuf, const LaneBase& lb, int kh, int ks) {
+    const char* a = kbuf + ((lb.k ^ (32 * ks)) + kh * 32 * Layout<uint16_t, D>::ROWB);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
 }
 template <int D>
-__device__ __forceinline__ f32x8 k_frag(const char* kb, const LaneOffsets<float, D>& o, int kh, int ks) {
+__device__ __forceinline__ f32x8 k_frag_f32(const char* kbuf, const LaneBase& lb, int kh, int ks) {
+    typedef Layout<float, D> Ly;
     const int rl = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
-    const char* row = kb + kh * 32 * Layout<float, D>::ROWB + o.krow;
-    const int f = swz<Layout<float, D>::CPR>(rl);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + o.kpos[ks]);
+    const char* row = kbuf + kh * 32 * Ly::ROWB + lb.k;
+    const int f = swz<Ly::CPR>(rl);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + (((4 * ks + 2 * hl) ^ f) * 16));
     const f32x4 b = *reinterpret_cast<const f32x4*>(row + (((4 * ks + 2 * hl + 1) ^ f) * 16));
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// V^T operand for d block db over keys [base, base+16): lane (d = 32 db + l%32,
-// half hl) gets keys base+4hl+{0..3} and base+8+4hl+{0..3}.
+// V^T operand for d block db over keys [base, base+16) of the V buffer at
+// `vbuf`: lane (d = 32 db + l%32, half hl) gets keys base+4hl+{0..3} and
+// base+8+4hl+{0..3}.
 template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const char* vb, const LaneOffsets<uint16_t, D>& o, int db, int base) {
+__device__ __forceinline__ bf16x8 v_frag_bf16(const char* vbuf, const LaneBase& lb, int db, int base) {
     constexpr int RB = Layout<uint16_t, D>::ROWB;
-    const char* p0 = vb + base * RB + o.vrow + o.vpos[db][0];
-    const char* p1 = vb + (base + 8) * RB + o.vrow + o.vpos[db][1];
+    const char* p0 = vbuf + ((lb.v ^ (64 * db)) + base * RB);
+    const char* p1 = vbuf + ((lb.v ^ (64 * db + 32)) + (base + 8) * RB);
     const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
     const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
     const i16x8 r = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     return __builtin_bit_cast(bf16x8, r);
 }
 template <int D>
-__device__ __forceinline__ f32x8 v_frag(const char* vb, const LaneOffsets<float, D>&, int db, int base) {
-    constexpr int RB = Layout<float, D>::ROWB;
+__device__ __forceinline__ f32x8 v_frag_f32(const char* vbuf, const LaneBase&, int db, int base) {
+    typedef Layout<float, D> Ly;
     const int rl = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
     const int d = db * 32 + rl;
     f32x8 r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int key = base + (e >> 2) * 8 + 4 * hl + (e & 3);
-        r[e] = *reinterpret_cast<const float*>(vb + key * RB + (((d >> 2) ^ swz<Layout<float, D>::CPR>(key)) * 16) +
-                                               (d & 3) * 4);
+        r[e] = *reinterpret_cast<const float*>(vbuf + key * Ly::ROWB +
+                                               (((d >> 2) ^ swz<Ly::CPR>(key)) * 16) + (d & 3) * 4);
     }
     return r;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag k_frag(const char* kbuf, const LaneBase& lb, int kh, int ks) {
+    if constexpr (sizeof(T) == 2) return k_frag_bf16<D>(kbuf, lb, kh, ks);
+    else return k_frag_f32<D>(kbuf, lb, kh, ks);
+}
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag v_frag(const char* vbuf, const LaneBase& lb, int db, int base) {
+    if constexpr (sizeof(T) == 2) return v_frag_bf16<D>(vbuf, lb, db, base);
+    else return v_frag_f32<D>(vbuf, lb, db, base);
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -293,7 +362,7 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-wave running state.
+// Per-wave running state (32 rows).
 template <typename T, int D>
 struct RowState {
     f32x16 oacc[D / 32];
@@ -301,42 +370,46 @@ struct RowState {
     float l_part;  // this lane's share of the normaliser
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void compute_step(const Buf<T, D>& buf, const Step& cur, const Params& p,
-                                             const LaneOffsets<T, D>& lo,
-                                             const typename Elem<T>::frag (&qf)[D / 16],
-                                             RowState<T, D>& rs, int pattern, int my_a, int i_row) {
-    typedef typename Elem<T>::frag Frag;
-    constexpr int NKS = D / 16;
-    constexpr int NDB = D / 32;
-    const int lane = threadIdx.x & 63;
-    const int hl = lane >> 5;
-
-    int mode;
-    if (cur.kind == 1) {
-        mode = kMaskColumns;
-    } else if (pattern == MI_ASHAPE) {
-        const bool full = cur.kb < my_a &&
-                          ((cur.kb * 64 + 63 < p.sink) || ((my_a - cur.kb) * 64 + 63 < p.local));
-        mode = full ? kMaskNone : kMaskAShape;
-    } else {
-        mode = cur.kb >= my_a ? kMaskCausal : kMaskNone;
+// Mask mode of a step for the query block `my_a`.
+__device__ __forceinline__ int step_mode(uint32_t w, const Params& p, int pattern, int my_a) {
+    if (step_col(w)) return kMaskColumns;
+    const int kb = step_kb(w);
+    if (pattern == MI_ASHAPE) {
+        const bool full = kb < my_a && ((kb * 64 + 63 < p.sink) || ((my_a - kb) * 64 + 63 < p.local));
+        return full ? kMaskNone : kMaskAShape;
     }
+    return kb >= my_a ? kMaskCausal : kMaskNone;
+}
 
-    // ---- S^T = K . Q^T, the two 32-key halves interleaved
-    f32x16 s[2];
+// S^T = K . Q^T for one step (the two 32-key halves interleaved).
+template <typename T, int D>
+__device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, const LaneBase& lb,
+                                          const typename Elem<T>::frag (&qf)[D / 16]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kh][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) mma32(s[kh], k_frag<D>(buf.k, lo, kh, ks), qf[ks]);
+        for (int kh = 0; kh < 2; ++kh) mma32(s[kh], k_frag<T, D>(kbuf, lb, kh, ks), qf[ks]);
+}
 
-    // ---- masks (element e of half kh is key 32 kh + 8 (e/4) + 4 hl + e%4)
+// Masks one row block's scores (element e of half kh is key 32 kh + 8 (e/4) +
+// 4 hl + e%4 of the step) and returns the row's scaled max over the step.
+// Column steps read each slot's key position from `cl`.
+__device__ __forceinline__ float mask_and_max(f32x16 (&s)[2], int mode, int kb, const int32_t* cl,
+                                              const Params& p, int i_row) {
+    const int hl = (threadIdx.x >> 5) & 1;
+    // Opaque copies: the phase code appears once per group, and without
+    // these the compiler merges the two copies' comparisons and hoists them
+    // to the top of the step, holding 32+ lane masks in scalar registers.
+    asm volatile("" : "+v"(i_row));
+    int hl4 = 4 * hl;
+    asm volatile("" : "+v"(hl4));
+    (void)hl;
     if (mode == kMaskCausal) {
-        const int lim = i_row - cur.kb * 64 - 4 * hl;  // keep key-local kl iff kl - 4hl <= lim
+        const int lim = i_row - kb * 64 - hl4;  // keep key-local kl iff kl - 4hl <= lim
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -345,13 +418,15 @@ __device__ __forceinline__ void compute_step(const Buf<T, D>& buf, const Step& c
                 s[kh][e] = (klc <= lim) ? s[kh][e] : -INFINITY;
             }
     } else if (mode == kMaskAShape) {
-        const int j0 = cur.kb * 64 + 4 * hl;
+        // key j = kb*64 + 4hl + klc: keep iff j <= i_row and (j < sink or i_row - j < local)
+        const int j0 = kb * 64 + hl4;
+        const int lim = i_row - j0, sl = p.sink - j0, ll = i_row - p.local - j0;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int j = j0 + kh * 32 + 8 * (e >> 2) + (e & 3);
-                const bool keep = (j <= i_row) && ((j < p.sink) || (i_row - j < p.local));
+                const int klc = kh * 32 + 8 * (e >> 2) + (e & 3);
+                const bool keep = (klc <= lim) && ((klc < sl) || (klc > ll));
                 s[kh][e] = keep ? s[kh][e] : -INFINITY;
             }
     } else if (mode == kMaskColumns) {
@@ -359,7 +434,7 @@ __device__ __forceinline__ void compute_step(const Buf<T, D>& buf, const Step& c
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int4 j4 = *reinterpret_cast<const int4*>(&buf.colpos[kh * 32 + 8 * q4 + 4 * hl]);
+                const int4 j4 = *reinterpret_cast<const int4*>(&cl[kh * 32 + 8 * q4 + hl4]);
                 const int jj[4] = {j4.x, j4.y, j4.z, j4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -368,83 +443,156 @@ __device__ __forceinline__ void compute_step(const Buf<T, D>& buf, const Step& c
                 }
             }
     }
-
-    // ---- online softmax (log2 domain, lazily raised max)
     float mx = -INFINITY;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-    mx = pair_max(mx) * p.c;
+    return pair_max(mx) * p.c;
+}
+
+// Raises the running max if the step's max exceeds it by more than 2^kLazy
+// (rare after the first steps).  The accumulator factor `alpha` is applied
+// in the next MFMA phase, before the step's P.V is added, so that the vector
+// phase never rewrites the accumulators.  Returns whether any row raised.
+template <typename T, int D>
+__device__ __forceinline__ bool raise_max(RowState<T, D>& rs, float mx, float& alpha) {
     const bool raise = mx > rs.m_run + kLazy;
-    if (__ballot(raise)) {
-        const float alpha = raise ? fast_exp2(rs.m_run - mx) : 1.f;  // 0 when m_run = -inf
-        rs.m_run = raise ? mx : rs.m_run;
-        rs.l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) rs.oacc[db][e] *= alpha;
-    }
+    alpha = raise ? fast_exp2(rs.m_run - mx) : 1.f;  // 0 when m_run = -inf
+    rs.m_run = raise ? mx : rs.m_run;
+    rs.l_part *= alpha;
+    return __ballot(raise) != 0;
+}
+
+// Probabilities of a step against the running max, as P.V operands.
+template <typename T, int D>
+__device__ __forceinline__ void probs(typename Elem<T>::frag (&pf)[2][2], const f32x16 (&s)[2],
+                                      RowState<T, D>& rs, float c) {
+    typedef typename Elem<T>::frag Frag;
     const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
     float sum = 0.f;
+    f32x16 pv[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const float pv = fast_exp2(fmaf(s[kh][e], p.c, -m_use));
-            s[kh][e] = pv;
-            sum += pv;
+            pv[kh][e] = fast_exp2(fmaf(s[kh][e], c, -m_use));
+            sum += pv[kh][e];
         }
     rs.l_part += sum;
-
-    // ---- O^T += V^T . P^T over 16-key chunks (half kh, part pp)
-    Frag pf[2][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) pf[kh][pp] = make_p_frag(s[kh], 8 * pp, (Frag*)nullptr);
+        for (int pp = 0; pp < 2; ++pp) pf[kh][pp] = make_p_frag(pv[kh], 8 * pp, (Frag*)nullptr);
+}
+
+// O^T += V^T . P^T over 16-key chunks (half kh, part pp).
+template <typename T, int D>
+__device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vbuf, const LaneBase& lb,
+                                              const typename Elem<T>::frag (&pf)[2][2]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                mma32(rs.oacc[db], v_frag<D>(buf.v, lo, db, kh * 32 + pp * 16), pf[kh][pp]);
+            for (int db = 0; db < D / 32; ++db)
+                mma32(rs.oacc[db], v_frag<T, D>(vbuf, lb, db, kh * 32 + pp * 16), pf[kh][pp]);
 }
+
+// Between phases a wavefront carries either its scores or its P operands,
+// never both: P is parked in the score registers.
+__device__ __forceinline__ void park_p(f32x16 (&s)[2], const bf16x8 (&pf)[2][2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const f32x4 w = __builtin_bit_cast(f32x4, pf[kh][pp]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[0][(kh * 2 + pp) * 4 + e] = w[e];
+        }
+}
+__device__ __forceinline__ void unpark_p(bf16x8 (&pf)[2][2], const f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = s[0][(kh * 2 + pp) * 4 + e];
+            pf[kh][pp] = __builtin_bit_cast(bf16x8, w);
+        }
+}
+__device__ __forceinline__ void park_p(f32x16 (&s)[2], const f32x8 (&pf)[2][2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[kh][pp * 8 + e] = pf[kh][pp][e];
+}
+__device__ __forceinline__ void unpark_p(f32x8 (&pf)[2][2], const f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[kh][pp][e] = s[kh][pp * 8 + e];
+}
+
+// Barrier that does not wait for outstanding global->LDS copies.
+__device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); }
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     typedef typename Elem<T>::frag Frag;
+    typedef Layout<T, D> Ly;
+    typedef Arena<T, D> Ar;
     constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
-    __shared__ Buf<T, D> buf0;
-    __shared__ Buf<T, D> buf1;
+    __shared__ __attribute__((aligned(1024))) char kbuf0[Ly::TILEB];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[Ly::TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[Ly::TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[Ly::TILEB];
+    __shared__ __attribute__((aligned(16))) int32_t cpos0[64];  // key positions of a column step's slots
+    __shared__ __attribute__((aligned(16))) int32_t cpos1[64];
+    extern __shared__ __attribute__((aligned(16))) char dyn[];
 
-    const int items = p.B * p.Hq * p.npairs;
+    const int items = p.B * p.Hq * p.nruns;
     const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.xcd_chunk);
     if (L >= items) return;
-    // longest items first: query-block pairs in descending order
-    const int pair = p.npairs - 1 - L / (p.B * p.Hq);
+    // longest items first: runs of query blocks in descending order
+    const int run = p.nruns - 1 - L / (p.B * p.Hq);
     const int bh = L % (p.B * p.Hq);
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int kvh = h / p.group;
     const int pattern = p.all_dense ? MI_DENSE : p.pattern[h];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int blk = wave >> 1;  // 0: block a0, 1: block a1
+    // wave-uniform: lets all per-wave control live in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;                    // ping-pong group
+    const int blk = 2 * grp + ((wave >> 1) & 1);  // query block of this wave in the run
     const int hl = lane >> 5;
     const int rl = lane & 31;
-    const int a0 = 2 * pair, a1 = a0 + 1;
-    const int has1 = a1 < p.nb;
+    const int a0 = run * kBlocks;
+    const int nblk = min(kBlocks, p.nb - a0);
     const int my_a = a0 + blk;
-    const bool active = blk == 0 || has1;
+    const bool active = blk < nblk;
     const int i_row = my_a * 64 + (wave & 1) * 32 + rl;
 
     const T* qbase = reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1;
-    const T* kbase = reinterpret_cast<const T*>(p.k) + b * p.ks0 + kvh * p.ks1;
-    const T* vbase = reinterpret_cast<const T*>(p.v) + b * p.vs0 + kvh * p.vs1;
+    const char* kbase = p.k + (b * p.ks0 + kvh * p.ks1) * (int64_t)sizeof(T);
+    const char* vbase = p.v + (b * p.vs0 + kvh * p.vs1) * (int64_t)sizeof(T);
+    const int64_t kstride = p.ks2 * (int64_t)sizeof(T), vstride = p.vs2 * (int64_t)sizeof(T);
+
+    const int64_t r0 = (int64_t)bh * p.nb + a0;
+    const int nsteps = build_steps<T, D>(dyn, p, pattern, r0, a0, nblk);
+    const int32_t* colsl = reinterpret_cast<const int32_t*>(dyn);
+    const uint32_t* steps = reinterpret_cast<const uint32_t*>(dyn + Ar::steps(p.cstride));
+    const int cstride = p.cstride;
+    auto fetch = [&](int t) -> uint32_t {
+        return t < nsteps ? (uint32_t)__builtin_amdgcn_readfirstlane(steps[t]) : kNoStep;
+    };
 
     Frag qf[NKS];
     if (active) {
@@ -455,30 +603,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) qf[s] = Frag{};
     }
-    LaneOffsets<T, D> lo;
-    lane_offsets<T, D>(lo, lane);
-
-    Walker wk{};
-    wk.a0 = a0; wk.a1 = a1; wk.has1 = has1;
-    if (pattern == MI_DENSE) {
-        wk.dense = 1;
-    } else {
-        const int64_t r0 = (int64_t)bh * p.nb + a0;
-        wk.L0 = p.block_idx + r0 * p.block_cap;
-        wk.n0 = min(max(p.block_count[r0], 0), p.block_cap);
-        if (has1) {
-            wk.L1 = p.block_idx + (r0 + 1) * p.block_cap;
-            wk.n1 = min(max(p.block_count[r0 + 1], 0), p.block_cap);
-        }
-        if (pattern == MI_VSLASH) {
-            wk.C0 = p.col_idx + r0 * p.col_cap;
-            wk.m0 = min(max(p.col_count[r0], 0), p.col_cap);
-            if (has1) {
-                wk.C1 = p.col_idx + (r0 + 1) * p.col_cap;
-                wk.m1 = min(max(p.col_count[r0 + 1], 0), p.col_cap);
-            }
-        }
-    }
+    const LaneBase lb = lane_base<T, D>(lane);
 
     RowState<T, D> rs;
 #pragma unroll
@@ -487,24 +612,73 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
         for (int e = 0; e < 16; ++e) rs.oacc[db][e] = 0.f;
     rs.m_run = -INFINITY;
     rs.l_part = 0.f;
-    const bool mine0 = active;
 
-    // Two buffers, used alternately; the loop body is written out for each so
-    // that the LDS reads of one never wait on the copies into the other.
-    Step cur = wk.next();
-    if (cur.kind >= 0) issue_step<T, D>(buf0, cur, wk, kbase, vbase, p.ks2, p.vs2, p.N);
-    while (cur.kind >= 0) {
-        Step nxt = wk.next();
-        __syncthreads();  // buf0 landed for every wave; buf1 is no longer read
-        if (nxt.kind >= 0) issue_step<T, D>(buf1, nxt, wk, kbase, vbase, p.ks2, p.vs2, p.N);
-        if (mine0 && ((cur.need >> blk) & 1))
-            compute_step<T, D>(buf0, cur, p, lo, qf, rs, pattern, my_a, i_row);
-        if (nxt.kind < 0) break;
-        cur = wk.next();
-        __syncthreads();  // buf1 landed; buf0 is no longer read
-        if (cur.kind >= 0) issue_step<T, D>(buf0, cur, wk, kbase, vbase, p.ks2, p.vs2, p.N);
-        if (mine0 && ((nxt.need >> blk) & 1))
-            compute_step<T, D>(buf1, nxt, p, lo, qf, rs, pattern, my_a, i_row);
+    auto needs = [&](uint32_t w) { return active && w != kNoStep && ((step_need(w) >> blk) & 1); };
+    f32x16 s[2];  // scores of the current step, or its parked P operands
+    float mx = -INFINITY;
+    float alpha = 1.f;     // accumulator factor of the last vector phase
+    bool rescale = false;  // some row of the wavefront raised its max
+
+    // Step t = 0..nsteps-1 (and one drain step); phase 2t: group 0 runs M(t),
+    // group 1 runs V(t-1); phase 2t+1: group 1 runs M(t), group 0 runs V(t).
+    // K(t) sits in K buffer t%2, V(t) in V buffer t%2; the copies of K(t+1)
+    // and V(t) are issued at the start of phase 2t and waited for at the end
+    // of phase 2t+1 (after every read of the buffers they overwrite).
+    uint32_t wprev = kNoStep, wcur = fetch(0), wnext = fetch(1);
+    // one step; the loop below unrolls it twice so that every buffer is a
+    // fixed LDS object in each copy
+    auto step = [&](int t, char* kcur, char* knext, char* vcur, const char* vprev, const int32_t* cpcur,
+                    int32_t* cpnext) __attribute__((always_inline)) {
+        if (wnext != kNoStep)
+            issue_rows<T, D>(knext, wnext, colsl + step_blk(wnext) * cstride + step_kb(wnext), cpnext, kbase,
+                             kstride);
+        if (wcur != kNoStep) issue_rows<T, D>(vcur, wcur, cpcur, nullptr, vbase, vstride);
+        const bool pv_need = needs(wprev);
+        const bool s_need = needs(wcur);
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph) {
+            if (ph == grp) {
+                // M(t): P.V of step t-1, then S of step t.  Opaque lane bases
+                // keep the operand addresses from being hoisted out of the loop.
+                LaneBase lbo = lb;
+                asm volatile("" : "+v"(lbo.k), "+v"(lbo.v));
+                if (pv_need) {
+                    if (rescale) {
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) rs.oacc[db][e] *= alpha;
+                    }
+                    Frag pf[2][2];
+                    unpark_p(pf, s);
+                    pv_accumulate<T, D>(rs, vprev, lbo, pf);
+                }
+                if (s_need) {
+                    s_compute<T, D>(s, kcur, lbo, qf);
+                    mx = mask_and_max(s, step_mode(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row);
+                }
+            } else if (grp == 1 ? pv_need : s_need) {
+                // V(t-1) for group 1, V(t) for group 0
+                rescale = raise_max<T, D>(rs, mx, alpha);
+                Frag pf[2][2];
+                probs<T, D>(pf, s, rs, p.c);
+                park_p(s, pf);
+            }
+            if (ph == 0) phase_barrier();
+        }
+        if (wcur == kNoStep) return false;
+        __syncthreads();  // K(t+1) and V(t) have landed; phase 2t+2 begins
+        wprev = wcur;
+        wcur = wnext;
+        wnext = fetch(t + 2);
+        return true;
+    };
+    if (wcur != kNoStep)
+        issue_rows<T, D>(kbuf0, wcur, colsl + step_blk(wcur) * cstride + step_kb(wcur), cpos0, kbase, kstride);
+    __syncthreads();
+    for (int t = 0;; t += 2) {
+        if (!step(t, kbuf0, kbuf1, vbuf0, vbuf1, cpos0, cpos1)) break;
+        if (!step(t + 1, kbuf1, kbuf0, vbuf1, vbuf0, cpos1, cpos0)) break;
     }
 
     if (!active) return;
@@ -530,17 +704,39 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
         const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
         p.lse[(int64_t)bh * p.N + i_row] = (l > 0.f) ? (m_use + __log2f(l)) * kLn2 : -INFINITY;
     }
-    (void)rl;
+    (void)Ly::ROWB;
+}
+
+template <typename T, int D>
+size_t lds_bytes_t(int nb, int cstride) {
+    return (size_t)Arena<T, D>::kStatic + (size_t)Arena<T, D>::bytes(nb, cstride);
 }
 
 template <typename T, int D>
 hipError_t launch_t(const Params& p, hipStream_t s) {
-    const int items = p.B * p.Hq * p.npairs;
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D>), dim3(items), dim3(kThreads), 0, s, p);
+    const int items = p.B * p.Hq * p.nruns;
+    const size_t dyn = lds_bytes_t<T, D>(p.nb, p.cstride) - Arena<T, D>::kStatic;
+    if (dyn + Arena<T, D>::kStatic > kAttnMaxLds) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D>), dim3(items), dim3(kThreads), dyn, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int attn_col_stride(const AttnArgs& a) {
+    bool any_vs = false;
+    for (int h = 0; h < a.Hq; ++h) any_vs |= !a.all_dense && a.pattern[h] == MI_VSLASH;
+    return any_vs ? (a.col_cap + 63) / 64 * 64 : 0;
+}
+
+size_t sparse_attn_lds_bytes(const AttnArgs& a) {
+    const int nb = a.N / 64, cs = attn_col_stride(a);
+    if (a.dtype == MI_BF16) return a.D == 128 ? lds_bytes_t<uint16_t, 128>(nb, cs) : lds_bytes_t<uint16_t, 64>(nb, cs);
+    return a.D == 128 ? lds_bytes_t<float, 128>(nb, cs) : lds_bytes_t<float, 64>(nb, cs);
+}
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     Params p{};
@@ -554,12 +750,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     p.vs0 = a.vs[0]; p.vs1 = a.vs[1]; p.vs2 = a.vs[2];
     p.os0 = a.os[0]; p.os1 = a.os[1]; p.os2 = a.os[2];
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nb = a.N / 64;
-    p.npairs = (p.nb + 1) / 2;
+    p.nruns = (p.nb + kBlocks - 1) / kBlocks;
     p.group = a.Hq / a.Hkv;
     p.c = a.scale * kLog2e;
     p.block_count = a.block_count; p.block_idx = a.block_idx;
     p.col_count = a.col_count; p.col_idx = a.col_idx;
     p.block_cap = a.block_cap; p.col_cap = a.col_cap;
+    p.cstride = attn_col_stride(a);
     p.sink = a.sink; p.local = a.local;
     p.all_dense = a.all_dense;
     p.xcd_chunk = p.group;
