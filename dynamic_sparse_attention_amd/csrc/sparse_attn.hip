@@ -23,8 +23,8 @@
 // lane pair (l, l^32).
 //
 // Ping-pong schedule.  A wavefront's work on step t is split into an MFMA
-// phase M(t) = {P.V of step t-1, S of step t, its mask and row max} and a
-// vector phase V(t) = {running-max update, exponentials, P}.  Phases are
+// phase M(t) = {P.V of step t-1, S of step t and its mask} and a vector
+// phase V(t) = {row max, running-max update, exponentials, P}.  Phases are
 // separated by workgroup barriers; group 0 runs M(t) while group 1 runs
 // V(t-1), then group 0 runs V(t) while group 1 runs M(t), so the two
 // wavefronts sharing a SIMD keep the matrix cores and the vector ALUs busy
@@ -32,9 +32,10 @@
 //
 // Staging: K and V rows go from global memory straight into LDS
 // (global_load_lds_dwordx4, 16 bytes per lane, 1 KiB of consecutive LDS per
-// wave instruction).  K and V each have two buffers; at the start of phase 2t
-// the copies of K(t+1) and V(t) are issued, and they are waited for at the
-// end of phase 2t+1.  Rows are stored unpadded; 16-byte chunk c of row r sits
+// wave instruction).  K and V each have two buffers.  A group issues copies
+// at the start of its vector phase, while the other group's MFMA phase keeps
+// the matrix cores busy: group 1 the copy of K(t+1) in phase 2t, group 0
+// that of V(t) in phase 2t+1; both are waited for at the end of phase 2t+1.  Rows are stored unpadded; 16-byte chunk c of row r sits
 // at position c ^ f(r), f(r) = 4(r%4) + (r/4)%4 (16-chunk rows), so that a K
 // operand read (16 lanes per LDS cycle: 16 consecutive rows, same chunk) and
 // a V transposed read (32 lanes per cycle: 4 rows x 4 chunks) each hit all 64
@@ -74,6 +75,7 @@ struct Params {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;  // 8 wavefronts, two groups of 4
 constexpr int kBlocks = 4;             // query blocks per work item
+constexpr int kIssueWaves = 4;         // wavefronts that issue a step's copies (one group)
 // The running max is only raised when a row's new max exceeds it by more
 // than this (log2 units); probabilities then stay below 2^kLazy, and the
 // result is unchanged because numerator and normaliser share the same max.
@@ -137,8 +139,10 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issues the global->LDS copies of one step's K (or V) rows into the LDS
-// buffer `dst`.  Wave instruction `idx` fills LDS chunks [64 idx, 64 idx + 64):
+// Issues wave instructions it0..it1-1 of the global->LDS copy of one step's
+// K (or V) rows into the LDS buffer `dst`; the four wavefronts of one group
+// (rank 0..3) share the copy, CPR/4 instructions each.  Wave instruction
+// `idx` fills LDS chunks [64 idx, 64 idx + 64):
 // lane l writes chunk 64 idx + l, i.e. row (64 idx + l) / CPR at position
 // (64 idx + l) % CPR, which holds source chunk position ^ f(row).  Tile rows
 // are addressed from a uniform base plus a 32-bit lane offset.  Gathered rows
@@ -147,17 +151,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // `tok_dst` for the mask and the V copy of the same step.
 template <typename T, int D>
 __device__ __forceinline__ void issue_rows(char* dst, uint32_t w, const int32_t* tok_src, int32_t* tok_dst,
-                                           const char* base, int64_t stride_b) {
-    typedef Layout<T, D> Ly;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                           const char* base, int64_t stride_b, int rank, int it0, int it1) {
+    const int lane = threadIdx.x & 63;
     const bool col = step_col(w);
     const char* tile = base + (int64_t)step_kb(w) * 64 * stride_b;
 #pragma unroll
-    for (int it = 0; it < Ly::CPR / kWaves; ++it) {
-        const int idx = it * kWaves + wave;
+    for (int it = it0; it < it1; ++it) {
+        const int idx = it * kIssueWaves + rank;
         const int cidx = idx * 64 + lane;
-        const int row = cidx / Ly::CPR, pos = cidx % Ly::CPR;
-        const int chunk = pos ^ swz<Ly::CPR>(row);
+        const int row = cidx / Layout<T, D>::CPR, pos = cidx % Layout<T, D>::CPR;
+        const int chunk = pos ^ swz<Layout<T, D>::CPR>(row);
         const char* src;
         if (!col) {
             src = tile + (uint32_t)(row * (int32_t)stride_b + chunk * 16);
@@ -393,13 +396,23 @@ __device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, cons
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) mma32(s[kh], k_frag<T, D>(kbuf, lb, kh, ks), qf[ks]);
+    // bf16 schedule: four operand reads ahead, then one MFMA per read, so
+    // that LDS latency hides behind the MFMA chain
+    if constexpr (sizeof(T) == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
 }
 
 // Masks one row block's scores (element e of half kh is key 32 kh + 8 (e/4) +
-// 4 hl + e%4 of the step) and returns the row's scaled max over the step.
+// 4 hl + e%4 of the step).
 // Column steps read each slot's key position from `cl`.
-__device__ __forceinline__ float mask_and_max(f32x16 (&s)[2], int mode, int kb, const int32_t* cl,
-                                              const Params& p, int i_row) {
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int mode, int kb, const int32_t* cl,
+                                            const Params& p, int i_row) {
     const int hl = (threadIdx.x >> 5) & 1;
     // Opaque copies: the phase code appears once per group, and without
     // these the compiler merges the two copies' comparisons and hoists them
@@ -443,12 +456,16 @@ __device__ __forceinline__ float mask_and_max(f32x16 (&s)[2], int mode, int kb, 
                 }
             }
     }
+}
+
+// The row's max over a step's scores, scaled to log2 units.
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2], float c) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-    return pair_max(mx) * p.c;
+    return pair_max(mx) * c;
 }
 
 // Raises the running max if the step's max exceeds it by more than 2^kLazy
@@ -464,26 +481,22 @@ __device__ __forceinline__ bool raise_max(RowState<T, D>& rs, float mx, float& a
     return __ballot(raise) != 0;
 }
 
-// Probabilities of a step against the running max, as P.V operands.
-template <typename T, int D>
-__device__ __forceinline__ void probs(typename Elem<T>::frag (&pf)[2][2], const f32x16 (&s)[2],
-                                      RowState<T, D>& rs, float c) {
+// Probabilities of one 32-key half of a step against the running max, as
+// P.V operands; returns their fp32 sum.
+template <typename T>
+__device__ __forceinline__ float probs_half(typename Elem<T>::frag (&pf)[2], const f32x16& s, float m_use,
+                                            float c) {
     typedef typename Elem<T>::frag Frag;
-    const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
     float sum = 0.f;
-    f32x16 pv[2];
+    f32x16 pv;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int e = 0; e < 16; ++e) {
+        pv[e] = fast_exp2(fmaf(s[e], c, -m_use));
+        sum += pv[e];
+    }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            pv[kh][e] = fast_exp2(fmaf(s[kh][e], c, -m_use));
-            sum += pv[kh][e];
-        }
-    rs.l_part += sum;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) pf[kh][pp] = make_p_frag(pv[kh], 8 * pp, (Frag*)nullptr);
+    for (int pp = 0; pp < 2; ++pp) pf[pp] = make_p_frag(pv, 8 * pp, (Frag*)nullptr);
+    return sum;
 }
 
 // O^T += V^T . P^T over 16-key chunks (half kh, part pp).
@@ -497,6 +510,16 @@ __device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vb
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 mma32(rs.oacc[db], v_frag<T, D>(vbuf, lb, db, kh * 32 + pp * 16), pf[kh][pp]);
+    // bf16 schedule: eight transposed reads (four operands) ahead, then one
+    // MFMA per operand
+    if constexpr (sizeof(T) == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    }
 }
 
 // Between phases a wavefront carries either its scores or its P operands,
@@ -615,24 +638,20 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
 
     auto needs = [&](uint32_t w) { return active && w != kNoStep && ((step_need(w) >> blk) & 1); };
     f32x16 s[2];  // scores of the current step, or its parked P operands
-    float mx = -INFINITY;
     float alpha = 1.f;     // accumulator factor of the last vector phase
     bool rescale = false;  // some row of the wavefront raised its max
 
     // Step t = 0..nsteps-1 (and one drain step); phase 2t: group 0 runs M(t),
     // group 1 runs V(t-1); phase 2t+1: group 1 runs M(t), group 0 runs V(t).
-    // K(t) sits in K buffer t%2, V(t) in V buffer t%2; the copies of K(t+1)
-    // and V(t) are issued at the start of phase 2t and waited for at the end
-    // of phase 2t+1 (after every read of the buffers they overwrite).
+    // K(t) sits in K buffer t%2, V(t) in V buffer t%2.  Group 1 issues the
+    // copy of K(t+1) at the start of phase 2t and group 0 that of V(t) at the
+    // start of phase 2t+1 (the buffers' last readers finished in phase
+    // 2t-1); every wave waits for its own copies at the end of phase 2t+1.
     uint32_t wprev = kNoStep, wcur = fetch(0), wnext = fetch(1);
     // one step; the loop below unrolls it twice so that every buffer is a
     // fixed LDS object in each copy
     auto step = [&](int t, char* kcur, char* knext, char* vcur, const char* vprev, const int32_t* cpcur,
                     int32_t* cpnext) __attribute__((always_inline)) {
-        if (wnext != kNoStep)
-            issue_rows<T, D>(knext, wnext, colsl + step_blk(wnext) * cstride + step_kb(wnext), cpnext, kbase,
-                             kstride);
-        if (wcur != kNoStep) issue_rows<T, D>(vcur, wcur, cpcur, nullptr, vbase, vstride);
         const bool pv_need = needs(wprev);
         const bool s_need = needs(wcur);
 #pragma unroll
@@ -655,14 +674,28 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
                 }
                 if (s_need) {
                     s_compute<T, D>(s, kcur, lbo, qf);
-                    mx = mask_and_max(s, step_mode(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row);
+                    mask_scores(s, step_mode(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row);
                 }
-            } else if (grp == 1 ? pv_need : s_need) {
-                // V(t-1) for group 1, V(t) for group 0
-                rescale = raise_max<T, D>(rs, mx, alpha);
-                Frag pf[2][2];
-                probs<T, D>(pf, s, rs, p.c);
-                park_p(s, pf);
+            } else {
+                // Vector phase: V(t-1) for group 1, V(t) for group 0.  The
+                // group entering it first issues one of the copies, while the
+                // other group keeps the matrix cores busy: K(t+1) by group 1
+                // in phase 2t, V(t) by group 0 in phase 2t+1.
+                constexpr int NI = Ly::CPR / kIssueWaves;
+                if (ph == 0) {
+                    if (wnext != kNoStep)
+                        issue_rows<T, D>(knext, wnext, colsl + step_blk(wnext) * cstride + step_kb(wnext), cpnext,
+                                         kbase, kstride, wave & 3, 0, NI);
+                } else {
+                    if (wcur != kNoStep) issue_rows<T, D>(vcur, wcur, cpcur, nullptr, vbase, vstride, wave & 3, 0, NI);
+                }
+                if (grp == 1 ? pv_need : s_need) {
+                    rescale = raise_max<T, D>(rs, row_max(s, p.c), alpha);
+                    const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
+                    Frag pf[2][2];
+                    rs.l_part += probs_half<T>(pf[0], s[0], m_use, p.c) + probs_half<T>(pf[1], s[1], m_use, p.c);
+                    park_p(s, pf);
+                }
             }
             if (ph == 0) phase_barrier();
         }
@@ -673,8 +706,9 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
         wnext = fetch(t + 2);
         return true;
     };
-    if (wcur != kNoStep)
-        issue_rows<T, D>(kbuf0, wcur, colsl + step_blk(wcur) * cstride + step_kb(wcur), cpos0, kbase, kstride);
+    if (wcur != kNoStep && grp == 1)
+        issue_rows<T, D>(kbuf0, wcur, colsl + step_blk(wcur) * cstride + step_kb(wcur), cpos0, kbase, kstride,
+                         wave & 3, 0, Ly::CPR / kIssueWaves);
     __syncthreads();
     for (int t = 0;; t += 2) {
         if (!step(t, kbuf0, kbuf1, vbuf0, vbuf1, cpos0, cpos1)) break;
