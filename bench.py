@@ -4,10 +4,13 @@ A step is one pass of the whole hot path over a resident synthetic layer:
 the Vertical-Slash / Block-Sparse estimates (with top-k), the index build and
 the sparse attention, all enqueued on one stream.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config c3|c5|c2|c4|c1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config c3|c5|c2|c4|c1] [--no-cpu-baseline] [--no-1m]
 
 Default workload: the LLaMA-3-8B-shaped Vertical-Slash layer at 128K tokens
-(32 query / 8 kv heads, d=128, bf16, budgets 1000 verticals / 6096 slashes).
+(32 query / 8 kv heads, d=128, bf16, budgets 1000 verticals / 6096 slashes);
+`value` is its ms/layer.  The same line also carries the 1M-token layer of the
+same shape (two timed steps) and, for both, the dense causal attention kernel
+of the library timed on the same inputs.
 """
 from __future__ import annotations
 
@@ -40,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dense", action="store_true", help="also time the dense causal comparator once")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense causal comparator")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token secondary measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
@@ -158,20 +162,13 @@ def cpu_baseline(w, data, plan, budget_s):
                        f"{elapsed:.1f} s of CPU time")}
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding by kv-head "
-                          "group is designed but not built", "n_gpus": args.gpus}))
-        sys.exit(2)
+def measure(w, steps, warmup, dense, keep=False):
+    """Generates the workload, runs `warmup` untimed and `steps` timed passes
+    of the hot path (events around each call, on the stream the library
+    launches on), and optionally times the dense comparator once."""
     import torch
     import dynamic_sparse_attention_amd as mi
     import workloads as W
-
-    w = W.WORKLOADS[args.config]
     log(f"[bench] generating {w.name} (N={w.seq_len}, Hq={w.heads_q}, Hkv={w.heads_kv})")
     t0 = time.time()
     data = W.generate(w)
@@ -185,19 +182,21 @@ def main():
 
     q, k, v = up(data["q"]), up(data["k"]), up(data["v"])
     pats = [int(p) for p in data["patterns"]]
+    if not keep:
+        data = {"patterns": data["patterns"]}
     plan = mi.LayerPlan(q, k, v, pats, last_q=w.last_q, n_vertical=w.n_vertical, n_slash=w.n_slash,
                         force_vertical=w.force_vertical, force_slash=w.force_slash,
                         top_blocks=w.top_blocks, sink=w.sink, local=w.local)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         plan.run()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
+    log(f"[bench] {w.name}: warmup done ({warmup} steps)")
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         e = ev[s]
         e[0].record(stream)
         plan.estimate()
@@ -208,28 +207,55 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    ms_step = (t_end - t_start) * 1e3 / args.steps
-    est_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    idx_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (estimate {est_ms:.3f}, index {idx_ms:.3f}, "
-        f"attention {att_ms:.3f})")
-
-    d = w.head_dim
-    tiles, ncols, flop, dense_flop = index_work(plan, d)
+    res = {"ms_step": (t_end - t_start) * 1e3 / steps,
+           "est_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+           "idx_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+           "att_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
+    log(f"[bench] {w.name}: {steps} steps: {res['ms_step']:.3f} ms/step (estimate {res['est_ms']:.3f}, "
+        f"index {res['idx_ms']:.3f}, attention {res['att_ms']:.3f})")
+    res["tiles"], res["cols"], res["flop"], res["dense_flop"] = index_work(plan, w.head_dim)
     nb = w.n_blocks
-    causal_tiles = w.batch * w.heads_q * nb * (nb + 1) // 2
-    achieved = flop / (att_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    res["causal_tiles"] = w.batch * w.heads_q * nb * (nb + 1) // 2
+    if dense:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        plan.attention(dense=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        plan.attention(dense=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1)
+        res["dense"] = {"ms": round(dms, 3),
+                        "tflops": round(4.0 * w.head_dim * 64 * 64 * res["causal_tiles"] / (dms * 1e-3) / 1e12, 2)}
+        log(f"[bench] {w.name}: dense causal attention {dms:.3f} ms")
+    return res, plan, data
 
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding by kv-head "
+                          "group is designed but not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import workloads as W
+
+    w = W.WORKLOADS[args.config]
+    r, plan, data = measure(w, args.steps, args.warmup, not args.no_dense, keep=not args.no_cpu_baseline)
+    d = w.head_dim
+    achieved = r["flop"] / (r["att_ms"] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     out = {
         "metric": METRIC,
-        "value": round(ms_step, 4),
+        "value": round(r["ms_step"], 4),
         "unit": "ms/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -242,27 +268,38 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name),
-                     "flop_per_launch": flop},
-        "kernels_ms": {"estimate": round(est_ms, 4), "build_index": round(idx_ms, 4),
-                       "attention": round(att_ms, 4)},
+                     "flop_per_launch": r["flop"]},
+        "kernels_ms": {"estimate": round(r["est_ms"], 4), "build_index": round(r["idx_ms"], 4),
+                       "attention": round(r["att_ms"], 4)},
         "mfma_tflops": round(achieved, 2),
-        "effective_dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
-        "index": {"tiles": tiles, "columns": ncols, "tile_density": round(tiles / causal_tiles, 4)},
+        "effective_dense_equiv_tflops": round(r["dense_flop"] / (r["ms_step"] * 1e-3) / 1e12, 2),
+        "index": {"tiles": r["tiles"], "columns": r["cols"],
+                  "tile_density": round(r["tiles"] / r["causal_tiles"], 4)},
     }
-    if args.dense:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        plan.attention(dense=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        plan.attention(dense=True)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1)
-        out["dense_comparator"] = {"ms": round(dms, 3),
-                                   "tflops": round(4.0 * d * 64 * 64 * causal_tiles / (dms * 1e-3) / 1e12, 2)}
+    if "dense" in r:
+        out["dense_comparator"] = r["dense"]
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, data, plan, args.cpu_seconds)
+    del plan, data
+    if not args.no_1m and args.config == "c3":
+        torch.cuda.empty_cache()
+        w5 = W.WORKLOADS["c5"]
+        r5, plan5, _ = measure(w5, 2, 1, not args.no_dense)
+        ach5 = r5["flop"] / (r5["att_ms"] * 1e-3) / 1e12
+        out["secondary"] = {
+            "workload": w5.name, "seq_len": w5.seq_len, "steps": 2, "warmup": 1,
+            "ms_per_layer": round(r5["ms_step"], 3),
+            "kernels_ms": {"estimate": round(r5["est_ms"], 3), "build_index": round(r5["idx_ms"], 3),
+                           "attention": round(r5["att_ms"], 3)},
+            "mfma_tflops": round(ach5, 2), "frac": round(ach5 / PEAK_BF16_TFLOPS, 4),
+            "index": {"tiles": r5["tiles"], "columns": r5["cols"],
+                      "tile_density": round(r5["tiles"] / r5["causal_tiles"], 4)},
+        }
+        if "dense" in r5:
+            out["secondary"]["dense_comparator"] = r5["dense"]
+            out["secondary"]["speedup_vs_dense_attention"] = round(r5["dense"]["ms"] / r5["ms_step"], 3)
+        del plan5
     print(json.dumps(out), flush=True)
 
 
