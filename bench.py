@@ -207,7 +207,9 @@ def measure(w, steps, warmup, dense, keep=False):
         e[3].record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
+    per_step = [e[0].elapsed_time(e[3]) for e in ev]
     res = {"ms_step": (t_end - t_start) * 1e3 / steps,
+           "median_ms": float(np.median(per_step)),
            "est_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
            "idx_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
            "att_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
@@ -256,6 +258,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_step"], 4),
+        "median_ms_per_step": round(r["median_ms"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

@@ -154,3 +154,33 @@ def test_sparse_prefill_validation():
     assert call(pat(5, 3, 3, 3), index_struct()) == 7
     assert call(None, o=None) == 1
     assert call(None, o=FAKE + 8) == 2
+
+
+def test_sparse_prefill_rejects_oversized_lds_and_strides():
+    """The attention workgroup keeps its step list and the column lists of a
+    run of query blocks in LDS: shapes beyond the 160 KiB an MI355X CU has are
+    rejected on the host (MI_ERR_SHAPE) before any launch, as are K/V token
+    strides whose 64-row span does not fit a 32-bit offset."""
+    l = mi.lib()
+    pat = ctypes.cast((ctypes.c_int32 * 4)(1, 1, 1, 1), ctypes.c_void_p)
+
+    def call(d, idx, why):
+        st = l.mi_sparse_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, pat, ctypes.byref(idx), 128, 4096,
+                                 FAKE, None, None, 0, None)
+        assert why in ctypes.string_at(l.mi_last_error()).decode()
+        return st
+    # 2M tokens: the step list alone needs 128 KiB next to 64 KiB of staging tiles
+    long = desc(seq_len=1 << 21)
+    long.q_stride[:] = (4 << 21) * 128, (1 << 21) * 128, 128
+    long.k_stride[:] = (2 << 21) * 128, (1 << 21) * 128, 128
+    long.v_stride[:] = long.k_stride[:]
+    long.o_stride[:] = long.q_stride[:]
+    assert call(long, index_struct(), "bytes of LDS") == 2
+    # 10000 columns per query block: 4 column lists of 40 KiB each
+    big_cols = index_struct()
+    big_cols.col_cap = 10000
+    assert call(desc(), big_cols, "bytes of LDS") == 2
+    # a token stride of 2^25 elements: 64 rows span 4 GiB
+    wide = desc(k_stride=(1 << 40, 1 << 32, 1 << 25))
+    assert call(wide, index_struct(), "strides too large") == 2
+
