@@ -4,18 +4,24 @@
 // 2407.02490, key idea: Vertical-Slash heads estimate their important
 // positions from the last last_q queries.
 //
-// Three launches, all over (batch, listed head, key chunk):
-//   1. rowstat_partial: per 1024-key chunk, each row's running max and
-//      normaliser (log2 domain) with bf16/fp32 MFMA scores;
+// Four launches:
+//   1. rowstat_partial (batch, listed head, 1024-key chunk): each row's
+//      running max and normaliser (log2 domain) with bf16/fp32 MFMA scores;
 //   2. rowstat_combine: merges the chunk partials of each row in a fixed
 //      order;
-//   3. scores: recomputes the scores of a chunk of keys, normalises them with
-//      the row statistics, stores the 64 x (C+64) probabilities in LDS and
-//      sums columns and diagonals.  Work item c owns slash offsets
-//      [cC, cC+C) and vertical keys [N-(c+1)C, N-cC); the diagonals of those
-//      offsets reach keys [N-(c+1)C-63, N-cC), so each item recomputes 64
-//      extra keys instead of exchanging partial sums.  Every output is written
-//      by one thread with a fixed summation order (deterministic).
+//   3. scores (batch, listed head, 128-key chunk c = keys [J0, J0+128),
+//      J0 = N-(c+1)*128): recomputes the chunk's scores, normalises them with
+//      the row statistics and stores them in LDS skewed by row: with
+//      L = last_q, P[r][j] (query i_r = N-L+r) sits at column
+//      (j - J0) + L-1 - r, so that a diagonal of the score matrix (offset
+//      o = i_r - j) is one column, x = N-1-J0-o.  Columns give the chunk's
+//      part of the slash sums of offsets [128c-(L-1), 128c+127]; the
+//      anti-diagonals give the complete vertical sums of its keys.  Offsets
+//      [128c, 128c+127] are written as partial sums; the offsets below go to
+//      the workspace (63 slots, L-1 of them non-zero);
+//   4. slash_combine adds those values of chunk c+1 into the top offsets of
+//      chunk c.
+// Every output is summed by one thread in a fixed order (deterministic).
 //
 // Score layout (MFMA result, transposed): S^T (32 keys x 32 rows) = K . Q^T.
 // Lane l holds query row (l%32) of row block rb and keys
@@ -27,8 +33,11 @@ namespace mi {
 namespace {
 
 constexpr int kChunk1 = 1024;  // keys per row-statistics work item
-constexpr int kChunk2 = 256;   // offsets (and vertical keys) per score work item
-constexpr int kPitch2 = kChunk2 + 64 + 4;  // LDS row pitch of the probability tile (floats)
+constexpr int kChunk2 = 128;   // keys per score work item (one 32-key unit per wavefront)
+constexpr int kSpill = 63;     // slash offsets a chunk contributes below its own range
+// LDS row pitch of the skewed probability tile (floats): 191 columns used; a
+// pitch of 194 puts the column of consecutive rows on consecutive banks.
+constexpr int kPitch2 = 194;
 
 struct VsP {
     const char* q;
@@ -44,6 +53,7 @@ struct VsP {
     float* sscore;
     int64_t srow_b, srow_h;  // score row strides (elements)
     int32_t score_by_head;   // 1: row index is the head id, 0: the list position
+    float* spill;            // [B*n_heads][nchunk2][kSpill] slash partials below each chunk's range
 };
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -112,11 +122,33 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
     load_q_rows<T, D>(p, qbase, rl, hl, qf);
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    for (int u = wave; u < kChunk1 / 32; u += 4) {
+    // K fragments of the next unit are loaded before the current unit's
+    // vector work, so their latency hides behind it
+    typedef typename Elem<T>::frag Frag;
+    Frag kf[D / 16];
+    auto load_unit = [&](int key0) {
+        const int key = key0 + rl;
+        const bool ok = key >= 0 && key < p.N;
+        const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) kf[s] = ok ? load_frag(krow + 16 * s) : Frag{};
+    };
+    int u = wave;
+    if (chunk * kChunk1 + u * 32 < p.N) load_unit(chunk * kChunk1 + u * 32);
+    for (; u < kChunk1 / 32; u += 4) {
         const int key0 = chunk * kChunk1 + u * 32;
         if (key0 >= p.N) break;
         f32x16 acc[2];
-        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf[s], qf[rb][s]);
+        const int nkey0 = key0 + 4 * 32;
+        if (u + 4 < kChunk1 / 32 && nkey0 < p.N) load_unit(nkey0);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const int r = rb * 32 + rl;
@@ -125,9 +157,9 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-                const float s = (r < p.last_q && j <= ir) ? acc[rb][e] * p.c : -INFINITY;
-                acc[rb][e] = s;
-                mx = fmaxf(mx, s);
+                const float sc = (r < p.last_q && j <= ir) ? acc[rb][e] * p.c : -INFINITY;
+                acc[rb][e] = sc;
+                mx = fmaxf(mx, sc);
             }
             const float M = fmaxf(m[rb], mx);
             if (M == -INFINITY) continue;
@@ -194,46 +226,72 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
         inv_l[rb] = rs[1] > 0.f ? 1.f / rs[1] : 0.f;
     }
 
-    const int J0 = p.N - chunk * kChunk2 - kChunk2 - 64;  // first key of the tile
-    for (int u = wave; u < (kChunk2 + 64) / 32; u += 4) {
-        const int key0 = J0 + u * 32;
-        f32x16 acc[2];
-        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+    // wavefront w: keys [J0 + 32w, J0 + 32w + 32); J0 < 0 only in the last
+    // chunk when N % 128 == 64 (those keys score zero)
+    const int J0 = p.N - (chunk + 1) * kChunk2;
+    const int key0 = J0 + wave * 32;
+    f32x16 acc[2];
+    unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int r = rb * 32 + rl;
-            const int ir = p.N - p.last_q + r;
-            float pv[16];
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = rb * 32 + rl;
+        if (r >= p.last_q) continue;  // rows past last_q are not queries
+        const int ir = p.N - p.last_q + r;
+        float* prow = &P[r * kPitch2 + p.last_q - 1 - r];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-                const bool ok = (r < p.last_q) && (j >= 0) && (j <= ir);
-                pv[e] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
-            }
-            float* dst = &P[r * kPitch2 + u * 32 + 4 * hl];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<f32x4*>(dst + 8 * q4) =
-                    f32x4{pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
+        for (int e = 0; e < 16; ++e) {
+            const int jl = wave * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);  // key - J0
+            const int j = J0 + jl;
+            const bool ok = (j >= 0) && (j <= ir);
+            prow[jl] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
         }
     }
     __syncthreads();
-    const int t = threadIdx.x;  // kChunk2 == blockDim
-    float* vrow = p.vscore + b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
-    float* srow = p.sscore + b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
-    const int j = J0 + 64 + t;
-    if (j >= 0) {
-        float acc = 0.f;
-        for (int r = 0; r < p.last_q; ++r) acc += P[r * kPitch2 + 64 + t];
-        vrow[j] = acc;
+    const int t = threadIdx.x;
+    const int Lq = p.last_q;
+    const int64_t row_off = b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
+    if (t < kChunk2) {
+        // vertical sum of key J0 + t: the anti-diagonal (r, t + L-1 - r)
+        const int j = J0 + t;
+        if (j >= 0) {
+            float a = 0.f;
+            for (int r = 0; r < Lq; ++r) a += P[r * kPitch2 + t + Lq - 1 - r];
+            p.vscore[row_off + j] = a;
+        }
+    } else {
+        // slash partials: column x holds offset o = N - 1 - J0 - x for rows
+        // r < L with 0 <= x - (L-1) + r < 128
+        for (int x = t - kChunk2; x < kChunk2 + kSpill; x += 256 - kChunk2) {
+            const int r0 = max(0, Lq - 1 - x), r1 = min(Lq, kChunk2 + Lq - 1 - x);
+            float a = 0.f;
+            for (int r = r0; r < r1; ++r) a += P[r * kPitch2 + x];
+            const int o = p.N - 1 - J0 - x;
+            if (x < kChunk2) {
+                if (o < p.N) p.sscore[row_off + o] = a;
+            } else {
+                p.spill[((int64_t)bl * p.nchunk2 + chunk) * kSpill + (x - kChunk2)] = a;
+            }
+        }
     }
-    const int o = chunk * kChunk2 + t;
-    if (o < p.N) {
-        float acc = 0.f;
-        const int base = kChunk2 + 64 - p.last_q - t;
-        for (int r = 0; r < p.last_q; ++r) acc += P[r * kPitch2 + base + r];
-        srow[o] = acc;
-    }
+}
+
+// Adds the spill of chunk c+1 (offsets [128c+65, 128c+127]) into chunk c's
+// partial slash sums; one thread per (row, chunk, offset).
+__global__ void __launch_bounds__(256) vs_slash_combine(VsP p) {
+    const int64_t total = (int64_t)p.B * p.n_heads * p.nchunk2 * kSpill;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= total) return;
+    const int k = (int)(g % kSpill);
+    const int64_t rc = g / kSpill;
+    const int chunk = (int)(rc % p.nchunk2);  // the spilling chunk c+1
+    const int bl = (int)(rc / p.nchunk2);
+    if (chunk == 0) return;  // offsets below 0 do not exist
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li];
+    const int J0 = p.N - (chunk + 1) * kChunk2;
+    const int o = p.N - 1 - J0 - (kChunk2 + k);
+    const int64_t row_off = b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
+    p.sscore[row_off + o] += p.spill[g];
 }
 
 template <typename T, int D>
@@ -247,6 +305,10 @@ hipError_t launch_t(VsP& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int n2 = p.B * p.n_heads * p.nchunk2;
     hipLaunchKernelGGL((vs_scores<T, D>), dim3(n2), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n3 = (int64_t)n2 * kSpill;
+    hipLaunchKernelGGL(vs_slash_combine, dim3((unsigned)((n3 + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -256,8 +318,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t vs_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_scores) {
     const size_t nchunk1 = (N + kChunk1 - 1) / kChunk1;
+    const size_t nchunk2 = (N + kChunk2 - 1) / kChunk2;
     size_t bytes = align256((size_t)B * n_heads * nchunk1 * 64 * 2 * sizeof(float));
     bytes += align256((size_t)B * n_heads * 64 * 2 * sizeof(float));
+    bytes += align256((size_t)B * n_heads * nchunk2 * kSpill * sizeof(float));
     if (!caller_scores) bytes += 2 * align256((size_t)B * n_heads * N * sizeof(float));
     return bytes;
 }
@@ -280,6 +344,8 @@ hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
     off += align256((size_t)a.B * a.n_heads * p.nchunk1 * 64 * 2 * sizeof(float));
     p.rowstat = reinterpret_cast<float*>(ws + off);
     off += align256((size_t)a.B * a.n_heads * 64 * 2 * sizeof(float));
+    p.spill = reinterpret_cast<float*>(ws + off);
+    off += align256((size_t)a.B * a.n_heads * p.nchunk2 * kSpill * sizeof(float));
     if (a.vscore != nullptr) {
         // caller rows [B, Hq, N], indexed by head id
         p.vscore = a.vscore;
