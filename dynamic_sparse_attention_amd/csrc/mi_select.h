@@ -7,7 +7,11 @@
 // select over 11/11/10-bit digits with an LDS histogram, then one ordered
 // pass keeps every key > T and the first `need` keys == T in index order, so
 // the output is ascending and independent of thread timing.  Histogram
-// counts are integer atomics, whose sums do not depend on order.
+// counts are integer atomics, whose sums do not depend on order.  The
+// ordered pass gives each wavefront a contiguous segment of candidates: one
+// counting sweep, one exchange of the per-wavefront counts through LDS, and
+// one writing sweep in which ballots order the members of each 64-candidate
+// chunk.
 #pragma once
 
 #include "mi_device.h"
@@ -24,6 +28,7 @@ constexpr uint32_t kForcedKey = 0xFFFFFFFFu;
 struct SelectSmem {
     uint32_t hist[2048];
     int32_t wave_tot[17];
+    int32_t seg_gt[16], seg_eq[16];  // per-wavefront counts of the ordered pass
     uint32_t found_digit;
     int32_t found_above;
 };
@@ -87,9 +92,19 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelectSmem& sm, uint32_
         const int nbins = pass == 2 ? 1024 : 2048;
         for (int i = threadIdx.x; i < 2048; i += NT) sm.hist[i] = 0u;
         __syncthreads();
-        for (int i = threadIdx.x; i < n; i += NT) {
-            const uint32_t kk = key(i);
-            if ((kk & pmask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & (nbins - 1)], 1u);
+        // eight independent loads per thread before their atomics, so that
+        // the loop is not bound by one memory latency per element
+        for (int i0 = threadIdx.x; i0 < n; i0 += 8 * NT) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * NT;
+                kk[u] = i < n ? key(i) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * NT < n && (kk[u] & pmask) == prefix)
+                    atomicAdd(&sm.hist[(kk[u] >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
         // thread t owns bins in descending order: positions [t*BPT, (t+1)*BPT)
@@ -136,20 +151,62 @@ __device__ void select_topk(KeyFn key, int n, int k, int budget, int32_t* out, S
     uint32_t T;
     int need;
     radix_threshold<NT>(key, n, k, sm, T, need);
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
+    const int seg = (n + NW * 64 - 1) / (NW * 64) * 64;  // candidates per wavefront
+    const int s0 = wave * seg, s1 = min(n, s0 + seg);
+    // sweep 1: counts of keys > T and == T in this wavefront's segment
+    // (four 64-candidate chunks loaded together)
+    int gt = 0, eq = 0;
+    for (int base = s0; base < s1; base += 256) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 64 * u + lane;
+            kk[u] = (i < s1) ? key(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 64 * u + lane;
+            gt += __popcll(__ballot(i < s1 && kk[u] > T));
+            eq += __popcll(__ballot(i < s1 && kk[u] == T));
+        }
+    }
+    if (lane == 0) {
+        sm.seg_gt[wave] = gt;
+        sm.seg_eq[wave] = eq;
+    }
+    __syncthreads();
+    int sel_base = 0, eq_before = 0;
+    for (int w = 0; w < wave; ++w) {
+        const int e = sm.seg_eq[w];
+        const int take = min(max(need - eq_before, 0), e);
+        sel_base += sm.seg_gt[w] + take;
+        eq_before += e;
+    }
+    const int eq_take = min(max(need - eq_before, 0), eq);  // first eq_take keys == T of the segment
+    // sweep 2: ordered writes
     int run_eq = 0, run_sel = 0;
-    for (int base = 0; base < n && run_sel < k; base += NT) {
-        const int i = base + threadIdx.x;
-        const uint32_t kk = (i < n) ? key(i) : 0u;
-        const bool gt = (i < n) && kk > T;
-        const bool eq = (i < n) && kk == T;
-        int eq_tot;
-        const int eq_before = block_flag_scan<NT>(eq, sm, eq_tot);
-        const bool sel = gt || (eq && run_eq + eq_before < need);
-        int sel_tot;
-        const int sel_before = block_flag_scan<NT>(sel, sm, sel_tot);
-        if (sel) out[run_sel + sel_before] = i;
-        run_eq += eq_tot;
-        run_sel += sel_tot;
+    for (int base = s0; base < s1; base += 256) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 64 * u + lane;
+            kk[u] = (i < s1) ? key(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 64 * u + lane;
+            const bool g = i < s1 && kk[u] > T;
+            const bool e = i < s1 && kk[u] == T;
+            const uint64_t me = __ballot(e);
+            const bool sel = g || (e && run_eq + __popcll(me & below) < eq_take);
+            const uint64_t ms = __ballot(sel);
+            if (sel) out[sel_base + run_sel + __popcll(ms & below)] = i;
+            run_eq += __popcll(me);
+            run_sel += __popcll(ms);
+        }
     }
     for (int i = k + threadIdx.x; i < budget; i += NT) out[i] = -1;
 }

@@ -9,8 +9,8 @@
 //      running max and normaliser (log2 domain) with bf16/fp32 MFMA scores;
 //   2. rowstat_combine: merges the chunk partials of each row in a fixed
 //      order;
-//   3. scores (batch, listed head, 128-key chunk c = keys [J0, J0+128),
-//      J0 = N-(c+1)*128): recomputes the chunk's scores, normalises them with
+//   3. scores (batch, listed head, group of eight 128-key chunks; chunk c =
+//      keys [J0, J0+128), J0 = N-(c+1)*128): recomputes the chunk's scores, normalises them with
 //      the row statistics and stores them in LDS skewed by row: with
 //      L = last_q, P[r][j] (query i_r = N-L+r) sits at column
 //      (j - J0) + L-1 - r, so that a diagonal of the score matrix (offset
@@ -35,6 +35,7 @@ namespace {
 constexpr int kChunk1 = 1024;  // keys per row-statistics work item
 constexpr int kChunk2 = 128;   // keys per score work item (one 32-key unit per wavefront)
 constexpr int kSpill = 63;     // slash offsets a chunk contributes below its own range
+constexpr int kChunksPerItem = 8;  // score chunks per workgroup (the Q rows are loaded once)
 // LDS row pitch of the skewed probability tile (floats): 191 columns used; a
 // pitch of 194 puts the column of consecutive rows on consecutive banks.
 constexpr int kPitch2 = 194;
@@ -204,10 +205,11 @@ __global__ void __launch_bounds__(64) vs_rowstat_combine(VsP p) {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) vs_scores(VsP p) {
     __shared__ float P[64 * kPitch2];
-    const int nitems = p.B * p.n_heads * p.nchunk2;
+    const int ngroups = (p.nchunk2 + kChunksPerItem - 1) / kChunksPerItem;
+    const int nitems = p.B * p.n_heads * ngroups;
     const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.group);
     if (L >= nitems) return;
-    const int chunk = L / (p.B * p.n_heads);
+    const int cg = L / (p.B * p.n_heads);
     const int bl = L % (p.B * p.n_heads);
     const int b = bl / p.n_heads, li = bl % p.n_heads;
     const int h = p.heads[li], kvh = h / p.group;
@@ -225,51 +227,68 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
         mrow[rb] = rs[0];
         inv_l[rb] = rs[1] > 0.f ? 1.f / rs[1] : 0.f;
     }
-
-    // wavefront w: keys [J0 + 32w, J0 + 32w + 32); J0 < 0 only in the last
-    // chunk when N % 128 == 64 (those keys score zero)
-    const int J0 = p.N - (chunk + 1) * kChunk2;
-    const int key0 = J0 + wave * 32;
-    f32x16 acc[2];
-    unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int r = rb * 32 + rl;
-        if (r >= p.last_q) continue;  // rows past last_q are not queries
-        const int ir = p.N - p.last_q + r;
-        float* prow = &P[r * kPitch2 + p.last_q - 1 - r];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int jl = wave * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);  // key - J0
-            const int j = J0 + jl;
-            const bool ok = (j >= 0) && (j <= ir);
-            prow[jl] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
-        }
-    }
-    __syncthreads();
     const int t = threadIdx.x;
     const int Lq = p.last_q;
     const int64_t row_off = b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
-    if (t < kChunk2) {
-        // vertical sum of key J0 + t: the anti-diagonal (r, t + L-1 - r)
-        const int j = J0 + t;
-        if (j >= 0) {
-            float a = 0.f;
-            for (int r = 0; r < Lq; ++r) a += P[r * kPitch2 + t + Lq - 1 - r];
-            p.vscore[row_off + j] = a;
+
+#pragma unroll 1
+    for (int ci = 0; ci < kChunksPerItem; ++ci) {
+        const int chunk = cg * kChunksPerItem + ci;
+        if (chunk >= p.nchunk2) break;
+        // wavefront w: keys [J0 + 32w, J0 + 32w + 32); J0 < 0 only in the last
+        // chunk when N % 128 == 64 (those keys score zero)
+        const int J0 = p.N - (chunk + 1) * kChunk2;
+        const int key0 = J0 + wave * 32;
+        f32x16 acc[2];
+        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+        if (ci > 0) __syncthreads();  // the previous chunk's sums have read the tile
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int r = rb * 32 + rl;
+            if (r >= Lq) continue;  // rows past last_q are not queries
+            const int ir = p.N - Lq + r;
+            float* prow = &P[r * kPitch2 + Lq - 1 - r];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int jl = wave * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);  // key - J0
+                const int j = J0 + jl;
+                const bool ok = (j >= 0) && (j <= ir);
+                prow[jl] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
+            }
         }
-    } else {
-        // slash partials: column x holds offset o = N - 1 - J0 - x for rows
-        // r < L with 0 <= x - (L-1) + r < 128
-        for (int x = t - kChunk2; x < kChunk2 + kSpill; x += 256 - kChunk2) {
-            const int r0 = max(0, Lq - 1 - x), r1 = min(Lq, kChunk2 + Lq - 1 - x);
-            float a = 0.f;
-            for (int r = r0; r < r1; ++r) a += P[r * kPitch2 + x];
-            const int o = p.N - 1 - J0 - x;
-            if (x < kChunk2) {
-                if (o < p.N) p.sscore[row_off + o] = a;
-            } else {
-                p.spill[((int64_t)bl * p.nchunk2 + chunk) * kSpill + (x - kChunk2)] = a;
+        __syncthreads();
+        if (t < kChunk2) {
+            // vertical sum of key J0 + t: the anti-diagonal (r, t + L-1 - r)
+            // (all 64 rows are read so the loads issue together; rows >= L hold
+            // no probabilities and are masked; every address stays in the tile)
+            const int j = J0 + t;
+            if (j >= 0) {
+                float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+                for (int r = 0; r < 64; ++r) {
+                    const float v = P[r * kPitch2 + t + Lq - 1 - r];
+                    a[r & 3] += (r < Lq) ? v : 0.f;
+                }
+                p.vscore[row_off + j] = (a[0] + a[1]) + (a[2] + a[3]);
+            }
+        } else {
+            // slash partials: column x holds offset o = N - 1 - J0 - x for rows
+            // r < L with 0 <= x - (L-1) + r < 128
+            for (int x = t - kChunk2; x < kChunk2 + kSpill; x += 256 - kChunk2) {
+                const int r0 = max(0, Lq - 1 - x), r1 = min(Lq, kChunk2 + Lq - 1 - x);
+                float ap[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+                for (int r = 0; r < 64; ++r) {
+                    const float v = P[r * kPitch2 + x];
+                    ap[r & 3] += (r >= r0 && r < r1) ? v : 0.f;
+                }
+                const float a = (ap[0] + ap[1]) + (ap[2] + ap[3]);
+                const int o = p.N - 1 - J0 - x;
+                if (x < kChunk2) {
+                    if (o < p.N) p.sscore[row_off + o] = a;
+                } else {
+                    p.spill[((int64_t)bl * p.nchunk2 + chunk) * kSpill + (x - kChunk2)] = a;
+                }
             }
         }
     }
@@ -303,11 +322,11 @@ hipError_t launch_t(VsP& p, hipStream_t s) {
     hipLaunchKernelGGL(vs_rowstat_combine, dim3(p.B * p.n_heads), dim3(64), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n2 = p.B * p.n_heads * p.nchunk2;
+    const int n2 = p.B * p.n_heads * ((p.nchunk2 + kChunksPerItem - 1) / kChunksPerItem);
     hipLaunchKernelGGL((vs_scores<T, D>), dim3(n2), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n3 = (int64_t)n2 * kSpill;
+    const int64_t n3 = (int64_t)p.B * p.n_heads * p.nchunk2 * kSpill;
     hipLaunchKernelGGL(vs_slash_combine, dim3((unsigned)((n3 + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
