@@ -105,6 +105,42 @@ def index_work(plan, d):
     return tiles, cols, flop, dense_flop
 
 
+def exact_pairs(plan, w):
+    """Attended (i, j) pairs of the exact per-element patterns, from the
+    selections the GPU made (host arithmetic, no attention):
+    Vertical-Slash |{j in V} u {i - o : o in S}| per row, summed as
+    sum(N - j) + sum(N - o) - #{(j, o) : j + o <= N - 1}; Block-Sparse the
+    causal pairs of the kept blocks; A-shape |{j <= i : j < sink or
+    i - j < local}|; dense N(N+1)/2."""
+    import torch
+    import workloads as W
+    B, Hq, N, _ = plan.q.shape
+    nb = N // 64
+    total = 0
+    vidx = plan.vidx.cpu().numpy() if plan.vidx is not None else None
+    sidx = plan.sidx.cpu().numpy() if plan.sidx is not None else None
+    bcnt = plan.bcnt.cpu().numpy() if plan.bcnt is not None else None
+    i = np.arange(N, dtype=np.int64)
+    # keys j < sink, plus the window [max(i - local + 1, sink), i]
+    ashape = int(np.sum(np.minimum(i + 1, w.sink) +
+                        np.maximum(0, i + 1 - np.maximum(i - w.local + 1, w.sink))))
+    for b in range(B):
+        for h, p in enumerate(plan.pat):
+            if p == W.VSLASH:
+                V = np.sort(vidx[b, h][vidx[b, h] >= 0]).astype(np.int64)
+                S = np.sort(sidx[b, h][sidx[b, h] >= 0]).astype(np.int64)
+                both = int(np.searchsorted(S, N - 1 - V, side="right").sum())
+                total += int((N - V).sum() + (N - S).sum()) - both
+            elif p == W.BSPARSE:
+                # every kept block is whole except the diagonal one (64*65/2 causal pairs)
+                total += int(bcnt[b, h].sum()) * 4096 - nb * (4096 - 2080)
+            elif p == W.ASHAPE:
+                total += ashape
+            else:
+                total += N * (N + 1) // 2
+    return total
+
+
 def cpu_baseline(w, data, plan, budget_s):
     """The oracle, untuned, on a bounded sample of the same layer, scaled to
     ms/layer: estimates + selection + index of a few heads, attention of a
@@ -216,6 +252,7 @@ def measure(w, steps, warmup, dense, keep=False):
     log(f"[bench] {w.name}: {steps} steps: {res['ms_step']:.3f} ms/step (estimate {res['est_ms']:.3f}, "
         f"index {res['idx_ms']:.3f}, attention {res['att_ms']:.3f})")
     res["tiles"], res["cols"], res["flop"], res["dense_flop"] = index_work(plan, w.head_dim)
+    res["exact_pairs"] = exact_pairs(plan, w)
     nb = w.n_blocks
     res["causal_tiles"] = w.batch * w.heads_q * nb * (nb + 1) // 2
     if dense:
@@ -231,6 +268,16 @@ def measure(w, steps, warmup, dense, keep=False):
                         "tflops": round(4.0 * w.head_dim * 64 * 64 * res["causal_tiles"] / (dms * 1e-3) / 1e12, 2)}
         log(f"[bench] {w.name}: dense causal attention {dms:.3f} ms")
     return res, plan, data
+
+
+def exact_summary(r, d):
+    """Exact-pattern work beside the issued tile work: how much the aligned
+    64x64 tiles and 64-key column chunks add, and the effective TFLOP/s
+    (4*d per attended pair over the attention time)."""
+    issued = r["tiles"] * 4096 + r["cols"] * 64
+    return {"attended_pairs": r["exact_pairs"], "issued_pairs": issued,
+            "tiling_overhead": round(issued / max(r["exact_pairs"], 1), 3),
+            "effective_tflops": round(4.0 * d * r["exact_pairs"] / (r["att_ms"] * 1e-3) / 1e12, 2)}
 
 
 def main():
@@ -278,6 +325,7 @@ def main():
         "effective_dense_equiv_tflops": round(r["dense_flop"] / (r["ms_step"] * 1e-3) / 1e12, 2),
         "index": {"tiles": r["tiles"], "columns": r["cols"],
                   "tile_density": round(r["tiles"] / r["causal_tiles"], 4)},
+        "exact_pattern": exact_summary(r, d),
     }
     if "dense" in r:
         out["dense_comparator"] = r["dense"]
@@ -298,6 +346,7 @@ def main():
             "mfma_tflops": round(ach5, 2), "frac": round(ach5 / PEAK_BF16_TFLOPS, 4),
             "index": {"tiles": r5["tiles"], "columns": r5["cols"],
                       "tile_density": round(r5["tiles"] / r5["causal_tiles"], 4)},
+            "exact_pattern": exact_summary(r5, w5.head_dim),
         }
         if "dense" in r5:
             out["secondary"]["dense_comparator"] = r5["dense"]

@@ -1,0 +1,48 @@
+"""Host-side arithmetic of bench.py: the exact-pattern pair counts it reports
+beside the issued tile work, checked against brute-force enumeration of the
+per-element patterns on tiny layers (no GPU)."""
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+import bench
+import workloads as W
+
+
+def brute(pattern, N, V=(), S=(), kept=None, sink=0, local=0):
+    n = 0
+    for i in range(N):
+        for j in range(i + 1):
+            if pattern == W.VSLASH:
+                ok = j in V or (i - j) in S
+            elif pattern == W.BSPARSE:
+                ok = (j // 64) in kept[i // 64]
+            elif pattern == W.ASHAPE:
+                ok = j < sink or i - j < local
+            else:
+                ok = True
+            n += ok
+    return n
+
+
+def test_exact_pairs_match_brute_force():
+    N, nb = 256, 4
+    rng = np.random.default_rng(0)
+    V = [0, 3, 100, 255]
+    S = [0, 1, 70, 129]
+    vidx = torch.full((1, 4, 6), -1, dtype=torch.int32)
+    sidx = torch.full((1, 4, 6), -1, dtype=torch.int32)
+    vidx[0, 1, :4] = torch.tensor(V)
+    sidx[0, 1, :4] = torch.tensor(S)
+    kept = [sorted({0, a} | set(int(x) for x in rng.integers(0, a + 1, 2))) for a in range(nb)]
+    bcnt = torch.zeros((1, 4, nb), dtype=torch.int32)
+    for a in range(nb):
+        bcnt[0, 2, a] = len(kept[a])
+    pats = [W.ASHAPE, W.VSLASH, W.BSPARSE, W.DENSE]
+    plan = SimpleNamespace(q=torch.zeros(1, 4, N, 8), pat=pats, vidx=vidx, sidx=sidx, bcnt=bcnt)
+    w = SimpleNamespace(sink=16, local=40)
+    got = bench.exact_pairs(plan, w)
+    want = (brute(W.ASHAPE, N, sink=16, local=40) + brute(W.VSLASH, N, V=set(V), S=set(S)) +
+            brute(W.BSPARSE, N, kept=kept) + brute(W.DENSE, N))
+    assert got == want
