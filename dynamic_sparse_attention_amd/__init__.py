@@ -30,7 +30,7 @@ STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_BUDGET", 4
           5: "MI_ERR_WORKSPACE", 6: "MI_ERR_LAUNCH", 7: "MI_ERR_PATTERN"}
 
 EXPORTS = ("mi_workspace_bytes", "mi_vs_estimate", "mi_block_estimate", "mi_build_index",
-           "mi_sparse_prefill", "mi_status_str", "mi_last_error")
+           "mi_sparse_prefill", "mi_attn_schedule", "mi_status_str", "mi_last_error")
 
 
 class MiError(RuntimeError):
@@ -67,6 +67,7 @@ _SIGS = {
                             ctypes.POINTER(MiIndex), _P]),
     "mi_sparse_prefill": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _P, ctypes.POINTER(MiIndex),
                                _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mi_attn_schedule": (_I, [ctypes.POINTER(MiAttnDesc), _P, _I, _I, _I, _P, _I]),
     "mi_status_str": (ctypes.c_char_p, [_I]),
     "mi_last_error": (ctypes.c_char_p, []),
 }
@@ -343,6 +344,8 @@ class LayerPlan:
         self.o = torch.empty_like(q)
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
         self.attn_desc = make_desc(q, k, v, self.o, scale=scale)
+        # attention item schedule (chunks of one kv group and pattern class)
+        self.attn_ws = _workspace(workspace_bytes(self.attn_desc, OP_SPARSE_PREFILL, 0), dev)
 
     def estimate(self, stream=None):
         kw, s, l = self.kw, _stream(stream), lib()
@@ -372,8 +375,8 @@ class LayerPlan:
         _check(lib().mi_sparse_prefill(ctypes.byref(self.attn_desc), _ptr(self.q), _ptr(self.k),
                                        _ptr(self.v), None if dense else ctypes.cast(self.pat_c, _P),
                                        None if dense else ctypes.byref(self.index_c), kw["sink"],
-                                       kw["local"], _ptr(self.o), _ptr(self.lse), None, 0,
-                                       _stream(stream)))
+                                       kw["local"], _ptr(self.o), _ptr(self.lse), _ptr(self.attn_ws),
+                                       self.attn_ws.numel(), _stream(stream)))
 
     def run(self, stream=None):
         self.estimate(stream)

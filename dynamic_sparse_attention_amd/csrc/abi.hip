@@ -118,7 +118,8 @@ size_t mi_workspace_bytes(const mi_attn_desc* d, int32_t op, int32_t p0, int32_t
         case MI_OP_VS_ESTIMATE: return mi::vs_workspace_bytes(d->batch, p0, d->seq_len, false);
         case MI_OP_BLOCK_ESTIMATE:
             return mi::bs_workspace_bytes(d->batch, p0, d->heads_kv, d->seq_len, d->head_dim, false);
-        case MI_OP_SPARSE_PREFILL: return 0;
+        case MI_OP_SPARSE_PREFILL:
+            return (mi::attn_schedule_bytes(d->batch, d->heads_q, d->heads_kv, d->seq_len) + 255) & ~size_t(255);
     }
     return 0;
 }
@@ -255,8 +256,6 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
                             const int32_t* head_pattern, const mi_index* idx, int32_t sink_tokens,
                             int32_t local_tokens, void* o, float* lse, void* ws, size_t ws_bytes,
                             void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     mi_status st = check_desc(d);
     if (st != MI_OK) return st;
     if (!q || !k || !v || !o) return fail(MI_ERR_NULL, "q, k, v or o is NULL");
@@ -303,7 +302,33 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
     if (lds > mi::kAttnMaxLds)
         return fail(MI_ERR_SHAPE, "attention needs %zu bytes of LDS (> %zu): seq_len or col_cap too large", lds,
                     mi::kAttnMaxLds);
-    return launched(mi::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ws) {
+        // the item schedule: copied into ws on the stream, read by the kernel
+        const std::vector<int32_t>& sched = mi::attn_schedule(a);
+        const size_t bytes = sched.size() * sizeof(int32_t);
+        if (ws_bytes < bytes) return fail(MI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, bytes);
+        if (hipMemcpyAsync(ws, sched.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+            return fail(MI_ERR_LAUNCH, "schedule upload failed: %s", hipGetErrorString(hipGetLastError()));
+        a.sched = static_cast<const int32_t*>(ws);
+        a.sched_len = (int32_t)sched.size();
+    }
+    return launched(mi::launch_sparse_attn(a, s));
+}
+
+int32_t mi_attn_schedule(const mi_attn_desc* d, const int32_t* head_pattern, int32_t sink_tokens,
+                         int32_t local_tokens, int32_t block_cap, int32_t* out, int32_t cap) {
+    if (check_desc(d) != MI_OK) return -1;
+    if (head_pattern && check_patterns(d, head_pattern) != MI_OK) return -1;
+    mi::AttnArgs a{};
+    a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.N = d->seq_len;
+    a.sink = sink_tokens; a.local = local_tokens; a.block_cap = block_cap;
+    a.all_dense = head_pattern ? 0 : 1;
+    for (int h = 0; h < d->heads_q; ++h) a.pattern[h] = head_pattern ? (uint8_t)head_pattern[h] : (uint8_t)MI_DENSE;
+    const std::vector<int32_t>& sched = mi::attn_schedule(a);
+    if (out)
+        for (int32_t i = 0; i < cap && i < (int32_t)sched.size(); ++i) out[i] = sched[i];
+    return (int32_t)sched.size();
 }
 
 }  // extern "C"

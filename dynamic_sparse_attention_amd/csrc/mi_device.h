@@ -112,6 +112,20 @@ __device__ __forceinline__ int chunked_xcd_remap(int w, int grid, int chunk) {
     return (t / chunk) * span + x * chunk + (t % chunk);
 }
 
+// As chunked_xcd_remap, but the chunk an XCD takes from a span rotates every
+// 8 spans: span s gives XCD x its chunk (x - s/8) mod 8.  Chunks of a span
+// that differ in work (query heads of different patterns) then spread over
+// all XCDs, while runs of 8 spans keep a chunk on one XCD (its L2).
+__device__ __forceinline__ int rotated_xcd_remap(int w, int grid, int chunk) {
+    const int span = 8 * chunk;
+    const int full = (grid / span) * span;
+    if (w >= full) return w;
+    const int t = w >> 3, x = w & 7;
+    const int s = t / chunk;
+    const int c = (x - (s >> 3)) & 7;
+    return s * span + c * chunk + (t % chunk);
+}
+
 // Load 8 consecutive elements (16 or 32 bytes) as an MFMA operand fragment.
 __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));

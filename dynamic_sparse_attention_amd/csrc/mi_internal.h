@@ -2,6 +2,8 @@
 // launchers in the other translation units.  Not part of the public ABI.
 #pragma once
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,8 +28,15 @@ struct AttnArgs {
     int32_t sink, local;
     int32_t all_dense;
     uint8_t pattern[MI_MAX_HEADS];
+    const int32_t* sched;  // device item schedule (NULL: the default order)
+    int32_t sched_len;     // entries (a multiple of 4)
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// Item schedule of the attention kernel (schedule.hip): bytes an upper bound
+// for any pattern set; the schedule itself is cached on the host for the life
+// of the process.
+size_t attn_schedule_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N);
+const std::vector<int32_t>& attn_schedule(const AttnArgs& a);
 // LDS of one attention workgroup: four K/V staging tiles, the four column
 // lists of a run of query blocks and its step list (grows with seq_len and
 // col_cap).

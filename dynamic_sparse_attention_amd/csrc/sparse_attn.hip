@@ -69,6 +69,8 @@ struct Params {
     int32_t sink, local;
     int32_t all_dense;
     int32_t xcd_chunk;
+    const int32_t* sched;  // item schedule: packed (b * Hq + h) * nruns + run, -1 = none
+    int32_t sched_len;
     uint8_t pattern[MI_MAX_HEADS];
 };
 
@@ -581,11 +583,21 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char dyn[];
 
     const int items = p.B * p.Hq * p.nruns;
-    const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.xcd_chunk);
-    if (L >= items) return;
-    // longest items first: runs of query blocks in descending order
-    const int run = p.nruns - 1 - L / (p.B * p.Hq);
-    const int bh = L % (p.B * p.Hq);
+    const int L = rotated_xcd_remap(blockIdx.x, gridDim.x, p.sched ? 4 : p.xcd_chunk);
+    int run, bh;
+    if (p.sched) {
+        // scheduled order: chunks of four items of one kv group and pattern
+        // class, longest first
+        const int it = ld_uniform(p.sched + L);
+        if (it < 0) return;
+        run = it % p.nruns;
+        bh = it / p.nruns;
+    } else {
+        if (L >= items) return;
+        // longest items first: runs of query blocks in descending order
+        run = p.nruns - 1 - L / (p.B * p.Hq);
+        bh = L % (p.B * p.Hq);
+    }
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int kvh = h / p.group;
     const int pattern = p.all_dense ? MI_DENSE : p.pattern[h];
@@ -748,7 +760,7 @@ size_t lds_bytes_t(int nb, int cstride) {
 
 template <typename T, int D>
 hipError_t launch_t(const Params& p, hipStream_t s) {
-    const int items = p.B * p.Hq * p.nruns;
+    const int items = p.sched ? p.sched_len : p.B * p.Hq * p.nruns;
     const size_t dyn = lds_bytes_t<T, D>(p.nb, p.cstride) - Arena<T, D>::kStatic;
     if (dyn + Arena<T, D>::kStatic > kAttnMaxLds) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D>),
@@ -794,6 +806,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     p.sink = a.sink; p.local = a.local;
     p.all_dense = a.all_dense;
     p.xcd_chunk = p.group;
+    p.sched = a.sched;
+    p.sched_len = a.sched_len;
     for (int i = 0; i < MI_MAX_HEADS; ++i) p.pattern[i] = a.pattern[i];
     if (a.dtype == MI_BF16) {
         return a.D == 128 ? launch_t<uint16_t, 128>(p, s) : launch_t<uint16_t, 64>(p, s);

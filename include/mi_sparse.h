@@ -95,7 +95,8 @@ typedef struct {
 
 /* Bytes of workspace an operation needs.  op = MI_OP_VS_ESTIMATE: p0 = number
  * of listed heads; MI_OP_BLOCK_ESTIMATE: p0 = number of listed heads;
- * MI_OP_SPARSE_PREFILL: 0 (no workspace).  Returns 0 for an invalid desc. */
+ * MI_OP_SPARSE_PREFILL: the item schedule (optional: with ws = NULL the
+ * kernel uses its default order).  Returns 0 for an invalid desc. */
 size_t mi_workspace_bytes(const mi_attn_desc* desc, int32_t op, int32_t p0, int32_t p1);
 
 /* Vertical-Slash index estimate (hotpaper.ai summary of arXiv 2407.02490, key
@@ -203,6 +204,20 @@ mi_status mi_sparse_prefill(const mi_attn_desc* desc, const void* q, const void*
                             const void* v, const int32_t* head_pattern, const mi_index* idx,
                             int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* The attention item schedule that mi_sparse_prefill copies into its ws
+ * (host call, no device work).  Items are runs of four 64-row query blocks
+ * of one (batch, query head), packed as (b * heads_q + h) * nruns + run with
+ * nruns = ceil(seq_len / 256); -1 marks padding.  Consecutive groups of four
+ * entries hold items of one kv group and one pattern class (Vertical-Slash
+ * and dense / A-shape / Block-Sparse), in run order, so that the heads a
+ * group of four runs together stream the same K/V tiles; groups are ordered
+ * by estimated length, longest first.  head_pattern as in mi_sparse_prefill
+ * (NULL = all dense); block_cap bounds the Block-Sparse estimate.  Writes
+ * min(cap, length) entries to out (may be NULL) and returns the length, or
+ * -1 for an invalid desc or pattern code. */
+int32_t mi_attn_schedule(const mi_attn_desc* desc, const int32_t* head_pattern, int32_t sink_tokens,
+                         int32_t local_tokens, int32_t block_cap, int32_t* out, int32_t cap);
 
 /* Static text of a status code. */
 const char* mi_status_str(mi_status s);

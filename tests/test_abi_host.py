@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import dynamic_sparse_attention_amd as mi
@@ -18,7 +19,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:mi_status|size_t|const char\*)\s+(mi_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:mi_status|size_t|int32_t|const char\*)\s+(mi_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
@@ -90,7 +91,9 @@ def test_workspace_sizes():
     bs = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_BLOCK_ESTIMATE, 2, 0)
     nb = 1024 // 64
     assert bs >= (2 * nb * 128 + 2 * nb * 128 + 2 * nb * nb) * 4
-    assert l.mi_workspace_bytes(ctypes.byref(d), mi.OP_SPARSE_PREFILL, 0, 0) == 0
+    # attention item schedule: one int32 per (batch, head, run of 4 query blocks) plus padding
+    pf = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_SPARSE_PREFILL, 0, 0)
+    assert pf >= 4 * 4 * (nb // 4) and pf % 256 == 0
     assert l.mi_workspace_bytes(ctypes.byref(desc(seq_len=10)), mi.OP_VS_ESTIMATE, 2, 0) == 0
 
 
@@ -184,3 +187,42 @@ def test_sparse_prefill_rejects_oversized_lds_and_strides():
     wide = desc(k_stride=(1 << 40, 1 << 32, 1 << 25))
     assert call(wide, index_struct(), "strides too large") == 2
 
+
+
+def test_attention_schedule_groups_heads_of_one_kv_group_and_class():
+    """The attention item schedule is a permutation of every (b, h, run) item
+    (plus -1 padding) in groups of four that share batch, kv group and
+    pattern class, in run order within a group, ordered longest first."""
+    l = mi.lib()
+    B, Hq, Hkv, N = 2, 8, 2, 64 * 37  # 10 runs, the last one partial
+    d = desc(batch=B, heads_q=Hq, heads_kv=Hkv, seq_len=N)
+    pats = [1, 0, 2, 1, 3, 3, 0, 2]
+    pat = ctypes.cast((ctypes.c_int32 * Hq)(*pats), ctypes.c_void_p)
+    n = l.mi_attn_schedule(ctypes.byref(d), pat, 128, 256, 8, None, 0)
+    buf = (ctypes.c_int32 * n)()
+    assert l.mi_attn_schedule(ctypes.byref(d), pat, 128, 256, 8, buf, n) == n
+    sched = np.array(buf[:], dtype=np.int64)
+    assert n % 4 == 0 and n * 4 <= l.mi_workspace_bytes(ctypes.byref(d), mi.OP_SPARSE_PREFILL, 0, 0)
+    nruns = (N // 64 + 3) // 4
+    items = sched[sched >= 0]
+    assert sorted(items.tolist()) == list(range(B * Hq * nruns))
+    cls = lambda p: {0: 1, 2: 2}.get(p, 0)  # A-shape, Block-Sparse, else (VS / dense)
+    group = Hq // Hkv
+    prev_est = None
+    for c in range(n // 4):
+        chunk = [int(x) for x in sched[4 * c: 4 * c + 4] if x >= 0]
+        assert chunk and all(x >= 0 for x in sched[4 * c: 4 * c + len(chunk)])  # padding only at the end
+        bh = [x // nruns for x in chunk]
+        runs = [x % nruns for x in chunk]
+        keys = {(x // Hq, (x % Hq) // group, cls(pats[x % Hq])) for x in bh}
+        assert len(keys) == 1
+        assert runs == sorted(runs, reverse=True)
+        first = runs[0]
+        span = min(N // 64, 4 * (first + 1))
+        k = cls(pats[bh[0] % Hq])
+        est = span if k == 0 else min(span, (128 + 63) // 64 + (256 + 126) // 64 + 4) if k == 1 else min(span, 4 * 8)
+        assert prev_est is None or est <= prev_est
+        prev_est = est
+    # dense comparator: every head in one class
+    n2 = l.mi_attn_schedule(ctypes.byref(d), None, 128, 256, 8, None, 0)
+    assert n2 == B * Hq * nruns
