@@ -267,9 +267,11 @@ def build_index(q, k, head_pattern: Sequence[int], vertical_idx=None, slash_idx=
 
 def sparse_prefill(q, k, v, head_pattern: Optional[Sequence[int]], index: Optional[Index],
                    sink: int = 128, local: int = 4096, scale: Optional[float] = None, out=None,
-                   lse=None, return_lse: bool = True, stream=None):
+                   lse=None, return_lse: bool = True, stream=None, schedule: bool = False):
     """Sparse attention per head pattern; head_pattern=None runs dense causal
-    attention on every head.  Returns (o, lse | None)."""
+    attention on every head.  schedule=True passes a workspace for the item
+    schedule (grouping the heads of a kv group by pattern class).  Returns
+    (o, lse | None)."""
     B, Hq, N, d = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -278,10 +280,12 @@ def sparse_prefill(q, k, v, head_pattern: Optional[Sequence[int]], index: Option
     desc = make_desc(q, k, v, out, scale=scale)
     pat = None if head_pattern is None else (ctypes.c_int32 * Hq)(*[int(p) for p in head_pattern])
     st = index.c_struct() if index is not None else None
+    ws = _workspace(workspace_bytes(desc, OP_SPARSE_PREFILL), q.device) if schedule else None
     _check(lib().mi_sparse_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                    None if pat is None else ctypes.cast(pat, _P),
                                    None if st is None else ctypes.byref(st), sink, local,
-                                   _ptr(out), _ptr(lse), None, 0, _stream(stream)))
+                                   _ptr(out), _ptr(lse), None if ws is None else _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
 
 

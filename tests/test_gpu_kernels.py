@@ -253,3 +253,29 @@ def test_index_is_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(*outs):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("n,hq,hkv,batch", [(64 * 45, 8, 2, 2), (64 * 13, 4, 4, 1)])
+def test_schedule_changes_order_not_results(n, hq, hkv, batch):
+    """With the item schedule (workspace given) the attention runs its items
+    in another order and on other XCDs; each item's arithmetic is unchanged,
+    so O and lse must be bit-identical to the default order, for a mix of all
+    four patterns with a ragged last run."""
+    say(f"schedule parity n={n} hq={hq} hkv={hkv} batch={batch}")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    q = torch.randn(batch, hq, n, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(batch, hkv, n, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(batch, hkv, n, 128, generator=g).to(torch.bfloat16).cuda()
+    pat = [W.VSLASH, W.ASHAPE, W.BSPARSE, W.DENSE, W.BSPARSE, W.VSLASH, W.DENSE, W.ASHAPE][:hq]
+    vs_h = [h for h, p in enumerate(pat) if p == W.VSLASH]
+    bs_h = [h for h, p in enumerate(pat) if p == W.BSPARSE]
+    vidx, sidx, _, _ = mi.vs_estimate(q, k, vs_h, 64, 90, 120)
+    bidx, bcnt, _ = mi.block_estimate(q, k, bs_h, 9)
+    idx = mi.build_index(q, k, pat, vidx, sidx, bidx, bcnt, 9, sink=100, local=700)
+    o1, l1 = mi.sparse_prefill(q, k, v, pat, idx, sink=100, local=700)
+    o2, l2 = mi.sparse_prefill(q, k, v, pat, idx, sink=100, local=700, schedule=True)
+    o3, l3 = mi.sparse_prefill(q, k, v, None, None)
+    o4, l4 = mi.sparse_prefill(q, k, v, None, None, schedule=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
