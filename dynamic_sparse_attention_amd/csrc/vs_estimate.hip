@@ -192,14 +192,23 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
     }
 }
 
-__global__ void __launch_bounds__(64) vs_rowstat_combine(VsP p) {
+// Four threads per row: thread q merges chunks q, q+4, q+8, ... in order,
+// then the four partials are merged in the order q = 0..3 (deterministic).
+__global__ void __launch_bounds__(256) vs_rowstat_combine(VsP p) {
+    __shared__ float sm[4][64][2];
     const int bl = blockIdx.x;
-    const int r = threadIdx.x;
+    const int r = threadIdx.x & 63, q = threadIdx.x >> 6;
     float M = -INFINITY, Ls = 0.f;
     const float* in = p.stats + ((int64_t)bl * p.nchunk1 * 64 + r) * 2;
-    for (int c = 0; c < p.nchunk1; ++c) merge_ml(M, Ls, in[(int64_t)c * 128], in[(int64_t)c * 128 + 1]);
-    p.rowstat[((int64_t)bl * 64 + r) * 2] = M;
-    p.rowstat[((int64_t)bl * 64 + r) * 2 + 1] = Ls;
+    for (int c = q; c < p.nchunk1; c += 4) merge_ml(M, Ls, in[(int64_t)c * 128], in[(int64_t)c * 128 + 1]);
+    sm[q][r][0] = M;
+    sm[q][r][1] = Ls;
+    __syncthreads();
+    if (q == 0) {
+        for (int k = 1; k < 4; ++k) merge_ml(M, Ls, sm[k][r][0], sm[k][r][1]);
+        p.rowstat[((int64_t)bl * 64 + r) * 2] = M;
+        p.rowstat[((int64_t)bl * 64 + r) * 2 + 1] = Ls;
+    }
 }
 
 template <typename T, int D>
@@ -319,7 +328,7 @@ hipError_t launch_t(VsP& p, hipStream_t s) {
     hipLaunchKernelGGL((vs_rowstat_partial<T, D>), dim3(n1), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(vs_rowstat_combine, dim3(p.B * p.n_heads), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(vs_rowstat_combine, dim3(p.B * p.n_heads), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n2 = p.B * p.n_heads * ((p.nchunk2 + kChunksPerItem - 1) / kChunksPerItem);
