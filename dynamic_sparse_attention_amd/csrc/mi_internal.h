@@ -79,8 +79,10 @@ struct TopkRows {
     int32_t score_by_head;
     int64_t srow_b, srow_h;
     TopkList list[2];
+    uint32_t* scratch;  // topk_scratch_bytes(2 * B * n_heads) of device memory
 };
 hipError_t launch_topk_rows(const TopkRows& t, hipStream_t s);
+size_t topk_scratch_bytes(int32_t rows);
 
 struct BsArgs {
     const void* q;

@@ -350,6 +350,7 @@ size_t vs_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_sco
     size_t bytes = align256((size_t)B * n_heads * nchunk1 * 64 * 2 * sizeof(float));
     bytes += align256((size_t)B * n_heads * 64 * 2 * sizeof(float));
     bytes += align256((size_t)B * n_heads * nchunk2 * kSpill * sizeof(float));
+    bytes += align256(topk_scratch_bytes(2 * B * n_heads));
     if (!caller_scores) bytes += 2 * align256((size_t)B * n_heads * N * sizeof(float));
     return bytes;
 }
@@ -374,6 +375,8 @@ hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
     off += align256((size_t)a.B * a.n_heads * 64 * 2 * sizeof(float));
     p.spill = reinterpret_cast<float*>(ws + off);
     off += align256((size_t)a.B * a.n_heads * p.nchunk2 * kSpill * sizeof(float));
+    uint32_t* topk_scratch = reinterpret_cast<uint32_t*>(ws + off);
+    off += align256(topk_scratch_bytes(2 * a.B * a.n_heads));
     if (a.vscore != nullptr) {
         // caller rows [B, Hq, N], indexed by head id
         p.vscore = a.vscore;
@@ -404,6 +407,7 @@ hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
     t.srow_b = p.srow_b; t.srow_h = p.srow_h;
     t.list[0] = {p.vscore, a.vertical_idx, a.n_vertical, a.force_vertical};
     t.list[1] = {p.sscore, a.slash_idx, a.n_slash, a.force_slash};
+    t.scratch = topk_scratch;
     return launch_topk_rows(t, s);
 }
 
