@@ -95,12 +95,17 @@ __device__ __forceinline__ void unit_scores(const VsP& p, const T* kbase, int ke
         for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
     const int key = key0 + rl;
     const bool ok = key >= 0 && key < p.N;
+    // every lane loads (a clamped, valid row) so the eight loads issue
+    // together; lanes outside [0, N) then use zero fragments
     const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
+    typename Elem<T>::frag kf[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        typename Elem<T>::frag kf = ok ? load_frag(krow + 16 * s) : typename Elem<T>::frag{};
+        if (!ok) kf[s] = typename Elem<T>::frag{};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf, qf[rb][s]);
+        for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf[s], qf[rb][s]);
     }
 }
 
@@ -132,7 +137,10 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
         const bool ok = key >= 0 && key < p.N;
         const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) kf[s] = ok ? load_frag(krow + 16 * s) : Frag{};
+        for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            if (!ok) kf[s] = Frag{};
     };
     int u = wave;
     if (chunk * kChunk1 + u * 32 < p.N) load_unit(chunk * kChunk1 + u * 32);
@@ -239,6 +247,11 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
     const int t = threadIdx.x;
     const int Lq = p.last_q;
     const int64_t row_off = b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
+    // Every chunk writes the same band of the tile (rows r < L, columns
+    // [L-1-r, L-1-r+128)); the rest is cleared once and stays zero, so the
+    // sums below run over all 64 rows without conditions.
+    for (int i = t; i < 64 * kPitch2; i += 256) P[i] = 0.f;
+    __syncthreads();
 
 #pragma unroll 1
     for (int ci = 0; ci < kChunksPerItem; ++ci) {
@@ -267,30 +280,23 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
         }
         __syncthreads();
         if (t < kChunk2) {
-            // vertical sum of key J0 + t: the anti-diagonal (r, t + L-1 - r)
-            // (all 64 rows are read so the loads issue together; rows >= L hold
-            // no probabilities and are masked; every address stays in the tile)
+            // vertical sum of key J0 + t: the anti-diagonal (r, t + L-1 - r);
+            // for rows r >= L the address falls on cleared cells (of row r, or
+            // for r > t + L-1 past the band of row r-1), all inside the tile
             const int j = J0 + t;
             if (j >= 0) {
                 float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
-                for (int r = 0; r < 64; ++r) {
-                    const float v = P[r * kPitch2 + t + Lq - 1 - r];
-                    a[r & 3] += (r < Lq) ? v : 0.f;
-                }
+                for (int r = 0; r < 64; ++r) a[r & 3] += P[r * kPitch2 + t + Lq - 1 - r];
                 p.vscore[row_off + j] = (a[0] + a[1]) + (a[2] + a[3]);
             }
         } else {
-            // slash partials: column x holds offset o = N - 1 - J0 - x for rows
-            // r < L with 0 <= x - (L-1) + r < 128
+            // slash partials: column x holds offset o = N - 1 - J0 - x
             for (int x = t - kChunk2; x < kChunk2 + kSpill; x += 256 - kChunk2) {
-                const int r0 = max(0, Lq - 1 - x), r1 = min(Lq, kChunk2 + Lq - 1 - x);
+                // cells of column x outside the band are cleared
                 float ap[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
-                for (int r = 0; r < 64; ++r) {
-                    const float v = P[r * kPitch2 + x];
-                    ap[r & 3] += (r >= r0 && r < r1) ? v : 0.f;
-                }
+                for (int r = 0; r < 64; ++r) ap[r & 3] += P[r * kPitch2 + x];
                 const float a = (ap[0] + ap[1]) + (ap[2] + ap[3]);
                 const int o = p.N - 1 - J0 - x;
                 if (x < kChunk2) {
