@@ -130,17 +130,17 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     // K fragments of the next unit are loaded before the current unit's
     // vector work, so their latency hides behind it
+    // (the in-range flag is applied where the MFMA reads the fragment, so
+    // that nothing waits for the loads before the current unit's work)
     typedef typename Elem<T>::frag Frag;
     Frag kf[D / 16];
+    bool kok = false;
     auto load_unit = [&](int key0) {
         const int key = key0 + rl;
-        const bool ok = key >= 0 && key < p.N;
-        const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
+        kok = key >= 0 && key < p.N;
+        const T* krow = kbase + (int64_t)(kok ? key : 0) * p.ks2 + 8 * hl;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            if (!ok) kf[s] = Frag{};
     };
     int u = wave;
     if (chunk * kChunk1 + u * 32 < p.N) load_unit(chunk * kChunk1 + u * 32);
@@ -153,9 +153,11 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
+        for (int s = 0; s < D / 16; ++s) {
+            const Frag a = kok ? kf[s] : Frag{};
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf[s], qf[rb][s]);
+            for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], a, qf[rb][s]);
+        }
         const int nkey0 = key0 + 4 * 32;
         if (u + 4 < kChunk1 / 32 && nkey0 < p.N) load_unit(nkey0);
 #pragma unroll
