@@ -5,8 +5,9 @@
 // positions from the last last_q queries.
 //
 // Four launches:
-//   1. rowstat_partial (batch, listed head, 1024-key chunk): each row's
-//      running max and normaliser (log2 domain) with bf16/fp32 MFMA scores;
+//   1. rowstat_partial (batch, set of up to four listed heads of one kv head,
+//      key chunk): each row's running max and normaliser (log2 domain) with
+//      bf16/fp32 MFMA scores, the K tiles staged once per set in LDS;
 //   2. rowstat_combine: merges the chunk partials of each row in a fixed
 //      order;
 //   3. scores (batch, listed head, group of eight 128-key chunks; chunk c =
@@ -26,19 +27,25 @@
 // Score layout (MFMA result, transposed): S^T (32 keys x 32 rows) = K . Q^T.
 // Lane l holds query row (l%32) of row block rb and keys
 // 8*(e/4) + 4*(l/32) + (e%4) of the 32-key unit.
+#include <algorithm>
+
 #include "mi_device.h"
 #include "mi_internal.h"
 
 namespace mi {
 namespace {
 
-constexpr int kChunk1 = 1024;  // keys per row-statistics work item
+// Row-statistics workgroups in flight (three per compute unit); the key
+// range of each set of heads is cut into about kRowstatWGs / sets chunks.
+constexpr int kRowstatWGs = 768;
 constexpr int kChunk2 = 128;   // keys per score work item (one 32-key unit per wavefront)
 constexpr int kSpill = 63;     // slash offsets a chunk contributes below its own range
 constexpr int kChunksPerItem = 8;  // score chunks per workgroup (the Q rows are loaded once)
 // LDS row pitch of the skewed probability tile (floats): 191 columns used; a
 // pitch of 194 puts the column of consecutive rows on consecutive banks.
 constexpr int kPitch2 = 194;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct VsP {
     const char* q;
@@ -50,6 +57,10 @@ struct VsP {
     float* stats;    // [B*n_heads][nchunk1][64] x (m, l)
     float* rowstat;  // [B*n_heads][64] x (m, l)
     int32_t nchunk1, nchunk2;
+    int32_t chunk1;  // keys per row-statistics chunk (a multiple of 64)
+    int32_t nsets;   // sets of listed heads that share a kv head (at most 4 each)
+    uint8_t set_n[MI_MAX_HEADS];
+    uint8_t set_li[MI_MAX_HEADS][4];  // list positions of each set's heads
     float* vscore;
     float* sscore;
     int64_t srow_b, srow_h;  // score row strides (elements)
@@ -83,122 +94,183 @@ __device__ __forceinline__ void load_q_rows(const VsP& p, const T* qbase, int rl
     }
 }
 
-// Scores of 32 keys [key0, key0+32) against the 64 row slots.  Keys outside
-// [0, N) contribute zero fragments (the caller masks them).
+// K fragments of the 32 keys [key0, key0+32): every lane loads (a clamped,
+// valid row) so that the loads issue together; lanes whose key lies outside
+// [0, N) get zero fragments in unit_mma.
 template <typename T, int D>
-__device__ __forceinline__ void unit_scores(const VsP& p, const T* kbase, int key0, int rl, int hl,
-                                            const typename Elem<T>::frag (&qf)[2][D / 16],
-                                            f32x16 (&acc)[2]) {
+__device__ __forceinline__ void unit_load(const VsP& p, const T* kbase, int key0, int rl, int hl,
+                                          typename Elem<T>::frag (&kf)[D / 16]) {
+    const int key = key0 + rl;
+    const bool ok = key >= 0 && key < p.N;
+    const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
+}
+
+// Scores of those 32 keys against the 64 row slots (out-of-range keys score
+// zero; the caller masks them).
+template <typename T, int D>
+__device__ __forceinline__ void unit_mma(const VsP& p, int key0, int rl, const typename Elem<T>::frag (&kf)[D / 16],
+                                         const typename Elem<T>::frag (&qf)[2][D / 16], f32x16 (&acc)[2]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
     const int key = key0 + rl;
     const bool ok = key >= 0 && key < p.N;
-    // every lane loads (a clamped, valid row) so the eight loads issue
-    // together; lanes outside [0, N) then use zero fragments
-    const T* krow = kbase + (int64_t)(ok ? key : 0) * p.ks2 + 8 * hl;
-    typename Elem<T>::frag kf[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        if (!ok) kf[s] = typename Elem<T>::frag{};
+        const typename Elem<T>::frag a = ok ? kf[s] : typename Elem<T>::frag{};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], kf[s], qf[rb][s]);
+        for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], a, qf[rb][s]);
+    }
+}
+
+// Row statistics over one key chunk for a set of up to four listed heads
+// that read the same kv head: the workgroup stages each 64-key K tile once
+// in LDS (global -> LDS copies, double-buffered) and
+// wavefront w scores it against the 64 estimate rows of the set's head w.
+// LDS rows are 16-byte chunks, chunk c of key row r stored at c ^ (r & 15),
+// so the fragment reads of 16 consecutive rows hit distinct banks.
+template <typename T, int D>
+struct KTile {
+    static constexpr int kRowBytes = D * (int)sizeof(T);
+    static constexpr int kCpr = kRowBytes / 16;           // 16-byte chunks per key row
+    static constexpr int kSwz = kCpr < 16 ? kCpr - 1 : 15;
+    static constexpr int kBytes = 64 * kRowBytes;
+    __device__ static int offset(int r, int c) { return r * kRowBytes + ((c ^ (r & kSwz)) << 4); }
+};
+
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag tile_frag(const char* tile, int r, int s, int hl) {
+    typedef KTile<T, D> Kt;
+    if constexpr (sizeof(T) == 2) {
+        // slots 16s + 8hl .. +8 of key row r: chunk 2s + hl
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + Kt::offset(r, 2 * s + hl)));
+    } else {
+        // slots 16s + 8hl .. +8 (32 bytes): chunks 4s + 2hl, +1
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tile + Kt::offset(r, 4 * s + 2 * hl));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(tile + Kt::offset(r, 4 * s + 2 * hl + 1));
+        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
 }
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
-    const int nitems = p.B * p.n_heads * p.nchunk1;
-    const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.group);
+    typedef KTile<T, D> Kt;
+    typedef typename Elem<T>::frag Frag;
+    __shared__ __attribute__((aligned(16))) char tiles[2][Kt::kBytes];
+    const int nitems = p.B * p.nsets * p.nchunk1;
+    const int L = blockIdx.x;
     if (L >= nitems) return;
-    // consecutive items: same chunk, consecutive listed heads (shared K in L2)
-    const int chunk = L / (p.B * p.n_heads);
-    const int bl = L % (p.B * p.n_heads);
-    const int b = bl / p.n_heads, li = bl % p.n_heads;
-    const int h = p.heads[li], kvh = h / p.group;
+    const int chunk = L % p.nchunk1;
+    const int bs = L / p.nchunk1;
+    const int b = bs / p.nsets, set = bs % p.nsets;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rl = lane & 31, hl = lane >> 5;
-    const T* qbase = reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1;
+    // list position of this wavefront's head (-1: the set has fewer heads)
+    const int li = wave < p.set_n[set] ? (int)p.set_li[set][wave] : -1;
+    const int kvh = p.heads[p.set_li[set][0]] / p.group;
     const T* kbase = reinterpret_cast<const T*>(p.k) + b * p.ks0 + kvh * p.ks1;
 
-    typename Elem<T>::frag qf[2][D / 16];
-    load_q_rows<T, D>(p, qbase, rl, hl, qf);
+    Frag qf[2][D / 16];
+    if (li >= 0) {
+        const int h = p.heads[li];
+        load_q_rows<T, D>(p, reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1, rl, hl, qf);
+    }
+    const int k_begin = chunk * p.chunk1;
+    const int k_end = min(p.N, k_begin + p.chunk1);
+    const int ntiles = (k_end - k_begin + 63) / 64;
+
+    // staging: global -> LDS copies (16 bytes per lane, 1 KiB of consecutive
+    // LDS per wavefront instruction); lane slot (row, pos) takes source chunk
+    // pos ^ (row & kSwz), which realises the swizzled layout
+    auto fetch = [&](char* tile, int ti) {
+        const int key0 = k_begin + 64 * ti;
+#pragma unroll
+        for (int i = 0; i < Kt::kCpr / 4; ++i) {
+            const int idx = i * 4 + wave;
+            const int cidx = idx * 64 + lane;
+            const int r = cidx / Kt::kCpr, pos = cidx % Kt::kCpr;
+            const int key = min(key0 + r, p.N - 1);  // rows past N are masked below
+            const char* src = reinterpret_cast<const char*>(kbase + (int64_t)key * p.ks2) + 16 * (pos ^ (r & Kt::kSwz));
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + idx * 1024), 16, 0, 0);
+        }
+    };
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    // K fragments of the next unit are loaded before the current unit's
-    // vector work, so their latency hides behind it
-    // (the in-range flag is applied where the MFMA reads the fragment, so
-    // that nothing waits for the loads before the current unit's work)
-    typedef typename Elem<T>::frag Frag;
-    Frag kf[D / 16];
-    bool kok = false;
-    auto load_unit = [&](int key0) {
-        const int key = key0 + rl;
-        kok = key >= 0 && key < p.N;
-        const T* krow = kbase + (int64_t)(kok ? key : 0) * p.ks2 + 8 * hl;
+    fetch(tiles[0], 0);
+    __syncthreads();
+#pragma unroll 1
+    for (int ti = 0; ti < ntiles; ++ti) {
+        if (ti + 1 < ntiles) fetch(tiles[(ti + 1) & 1], ti + 1);
+        const char* tile = tiles[ti & 1];
+        if (li >= 0) {
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) kf[s] = load_frag(krow + 16 * s);
-    };
-    int u = wave;
-    if (chunk * kChunk1 + u * 32 < p.N) load_unit(chunk * kChunk1 + u * 32);
-    for (; u < kChunk1 / 32; u += 4) {
-        const int key0 = chunk * kChunk1 + u * 32;
-        if (key0 >= p.N) break;
-        f32x16 acc[2];
+            for (int u = 0; u < 2; ++u) {
+                const int key0 = k_begin + 64 * ti + 32 * u;
+                f32x16 acc[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+                    for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const Frag a = kok ? kf[s] : Frag{};
+                for (int s = 0; s < D / 16; ++s) {
+                    const Frag a = tile_frag<T, D>(tile, 32 * u + rl, s, hl);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], a, qf[rb][s]);
-        }
-        const int nkey0 = key0 + 4 * 32;
-        if (u + 4 < kChunk1 / 32 && nkey0 < p.N) load_unit(nkey0);
+                    for (int rb = 0; rb < 2; ++rb) mma32(acc[rb], a, qf[rb][s]);
+                }
+                // units that end before the first estimate row's position need
+                // no mask (wave-uniform); the scale is positive, so the raw
+                // maximum scales to the scaled one
+                const bool open = key0 + 31 <= p.N - p.last_q;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int r = rb * 32 + rl;
-            const int ir = p.N - p.last_q + r;
-            float mx = -INFINITY;
+                for (int rb = 0; rb < 2; ++rb) {
+                    const int r = rb * 32 + rl;
+                    const int ir = p.N - p.last_q + r;
+                    if (open && rb * 32 + 31 < p.last_q) {
+                        float mx = acc[rb][0];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-                const float sc = (r < p.last_q && j <= ir) ? acc[rb][e] * p.c : -INFINITY;
-                acc[rb][e] = sc;
-                mx = fmaxf(mx, sc);
+                        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[rb][e]);
+                        const float M = fmaxf(m[rb], mx * p.c);
+                        float sum = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[rb][e], p.c, -M));
+                        l[rb] = l[rb] * fast_exp2(m[rb] - M) + sum;
+                        m[rb] = M;
+                        continue;
+                    }
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+                        const float sc = (r < p.last_q && j <= ir && j < k_end) ? acc[rb][e] * p.c : -INFINITY;
+                        acc[rb][e] = sc;
+                        mx = fmaxf(mx, sc);
+                    }
+                    const float M = fmaxf(m[rb], mx);
+                    if (M == -INFINITY) continue;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sum += fast_exp2(acc[rb][e] - M);
+                    l[rb] = l[rb] * fast_exp2(m[rb] - M) + sum;
+                    m[rb] = M;
+                }
             }
-            const float M = fmaxf(m[rb], mx);
-            if (M == -INFINITY) continue;
-            float sum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sum += fast_exp2(acc[rb][e] - M);
-            l[rb] = l[rb] * fast_exp2(m[rb] - M) + sum;
-            m[rb] = M;
         }
+        __syncthreads();  // waits for this wavefront's copies, then for all
     }
-    // lane pair (l, l^32) share a row; then 4 waves through LDS
-    __shared__ float sm_m[4][64], sm_l[4][64];
+    if (li < 0) return;
+    // lanes l and l^32 hold the same row
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         merge_ml(m[rb], l[rb], swap32(m[rb]), swap32(l[rb]));
         if (hl == 0) {
-            sm_m[wave][rb * 32 + rl] = m[rb];
-            sm_l[wave][rb * 32 + rl] = l[rb];
+            const int bl = b * p.n_heads + li;
+            float* out = p.stats + (((int64_t)bl * p.nchunk1 + chunk) * 64 + rb * 32 + rl) * 2;
+            out[0] = m[rb];
+            out[1] = l[rb];
         }
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int r = threadIdx.x;
-        float M = sm_m[0][r], Ls = sm_l[0][r];
-        for (int w = 1; w < 4; ++w) merge_ml(M, Ls, sm_m[w][r], sm_l[w][r]);
-        float* out = p.stats + (((int64_t)bl * p.nchunk1 + chunk) * 64 + r) * 2;
-        out[0] = M;
-        out[1] = Ls;
     }
 }
 
@@ -239,12 +311,12 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
 
     typename Elem<T>::frag qf[2][D / 16];
     load_q_rows<T, D>(p, qbase, rl, hl, qf);
-    float mrow[2], inv_l[2];
+    // p = 2^(s*c - m) / l = 2^(s*c - (m + log2 l)); l >= 1 for every real row
+    float mrow[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const float* rs = p.rowstat + ((int64_t)bl * 64 + rb * 32 + rl) * 2;
-        mrow[rb] = rs[0];
-        inv_l[rb] = rs[1] > 0.f ? 1.f / rs[1] : 0.f;
+        mrow[rb] = rs[1] > 0.f ? rs[0] + __log2f(rs[1]) : 0.f;
     }
     const int t = threadIdx.x;
     const int Lq = p.last_q;
@@ -263,8 +335,10 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
         // chunk when N % 128 == 64 (those keys score zero)
         const int J0 = p.N - (chunk + 1) * kChunk2;
         const int key0 = J0 + wave * 32;
+        typename Elem<T>::frag kf[D / 16];
+        unit_load<T, D>(p, kbase, key0, rl, hl, kf);
         f32x16 acc[2];
-        unit_scores<T, D>(p, kbase, key0, rl, hl, qf, acc);
+        unit_mma<T, D>(p, key0, rl, kf, qf, acc);
         if (ci > 0) __syncthreads();  // the previous chunk's sums have read the tile
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -272,12 +346,20 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
             if (r >= Lq) continue;  // rows past last_q are not queries
             const int ir = p.N - Lq + r;
             float* prow = &P[r * kPitch2 + Lq - 1 - r];
+            if (key0 >= 0 && key0 + 31 <= p.N - Lq) {  // wave-uniform: no masked key
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jl = wave * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);  // key - J0
+                    prow[jl] = fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb]));
+                }
+                continue;
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int jl = wave * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);  // key - J0
                 const int j = J0 + jl;
                 const bool ok = (j >= 0) && (j <= ir);
-                prow[jl] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) * inv_l[rb] : 0.f;
+                prow[jl] = ok ? fast_exp2(fmaf(acc[rb][e], p.c, -mrow[rb])) : 0.f;
             }
         }
         __syncthreads();
@@ -332,7 +414,7 @@ __global__ void __launch_bounds__(256) vs_slash_combine(VsP p) {
 
 template <typename T, int D>
 hipError_t launch_t(VsP& p, hipStream_t s) {
-    const int n1 = p.B * p.n_heads * p.nchunk1;
+    const int n1 = p.B * p.nsets * p.nchunk1;
     hipLaunchKernelGGL((vs_rowstat_partial<T, D>), dim3(n1), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -353,7 +435,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 size_t vs_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_scores) {
-    const size_t nchunk1 = (N + kChunk1 - 1) / kChunk1;
+    const size_t nchunk1 = std::min<size_t>(N / 64, kRowstatWGs);  // bound of the launcher's count
     const size_t nchunk2 = (N + kChunk2 - 1) / kChunk2;
     size_t bytes = align256((size_t)B * n_heads * nchunk1 * 64 * 2 * sizeof(float));
     bytes += align256((size_t)B * n_heads * 64 * 2 * sizeof(float));
@@ -373,7 +455,28 @@ hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
     p.n_heads = a.n_heads; p.last_q = a.last_q;
     p.c = a.scale * kLog2e;
     for (int i = 0; i < a.n_heads; ++i) p.heads[i] = a.heads[i];
-    p.nchunk1 = (a.N + kChunk1 - 1) / kChunk1;
+    // sets of up to four listed heads per kv head, in list order
+    {
+        int open_set[MI_MAX_HEADS];
+        for (int g = 0; g < a.Hkv; ++g) open_set[g] = -1;
+        p.nsets = 0;
+        for (int li = 0; li < a.n_heads; ++li) {
+            const int g = a.heads[li] / p.group;
+            int& st = open_set[g];
+            if (st < 0 || p.set_n[st] == 4) {
+                st = p.nsets++;
+                p.set_n[st] = 0;
+            }
+            p.set_li[st][p.set_n[st]++] = (uint8_t)li;
+        }
+    }
+    {
+        const int nb = a.N / 64;
+        int want = (kRowstatWGs + a.B * p.nsets - 1) / (a.B * p.nsets);
+        want = std::max(1, std::min(want, nb));
+        p.chunk1 = (nb + want - 1) / want * 64;
+        p.nchunk1 = (a.N + p.chunk1 - 1) / p.chunk1;
+    }
     p.nchunk2 = (a.N + kChunk2 - 1) / kChunk2;
     char* ws = static_cast<char*>(a.ws);
     size_t off = 0;

@@ -166,6 +166,30 @@ def test_vs_estimate(dtype, d, n, last_q, nv, ns, fv, fs):
     assert not vsc[0, 2].any() and not vidx[0, 2].any()  # unlisted head untouched
 
 
+@pytest.mark.parametrize("hq,hkv,batch,heads", [
+    (12, 1, 1, [0, 1, 2, 5, 7, 9, 11]),   # seven heads of one kv head: two sets
+    (3, 3, 2, [0, 2]),                    # one head per kv head, batch 2
+    (8, 2, 1, list(range(8))),            # full sets
+])
+def test_vs_estimate_head_sets(hq, hkv, batch, heads):
+    """Row statistics share each staged K tile among the listed heads of one
+    kv head (sets of at most four): every grouping gives the oracle's scores."""
+    say(f"vs_estimate head sets hq={hq} hkv={hkv} batch={batch} heads={heads}")
+    n, d, last_q, nv, ns = 64 * 21, 128, 64, 30, 50
+    _, (q, k, _), (q64, k64, _) = _inputs(13, hq, hkv, n, d, "bf16", batch=batch)
+    vidx, sidx, vsc, ssc = mi.vs_estimate(q, k, heads, last_q, nv, ns, 1, 1)
+    torch.cuda.synchronize()
+    vsc, ssc, vidx, sidx = f64(vsc), f64(ssc), vidx.cpu().numpy(), sidx.cpu().numpy()
+    g = hq // hkv
+    for b in range(batch):
+        for h in heads:
+            rv, rs = O.vs_estimate(q64[b, h], k64[b, h // g], d ** -0.5, last_q)
+            assert_scores_close(vsc[b, h], rv, f"vertical b{b} h{h}")
+            assert_scores_close(ssc[b, h], rs, f"slash b{b} h{h}")
+            check_selection(vidx[b, h], vsc[b, h], rv, nv, range(1), f"vertical b{b} h{h}")
+            check_selection(sidx[b, h], ssc[b, h], rs, ns, range(1), f"slash b{b} h{h}")
+
+
 def test_vs_estimate_without_score_outputs_is_identical():
     say("vs_estimate workspace scores")
     _, (q, k, _), _ = _inputs(12, 2, 1, 1024, 128, "bf16")
