@@ -11,8 +11,9 @@
 //   2. rowstat_combine: merges the chunk partials of each row in a fixed
 //      order;
 //   3. scores (batch, listed head, group of eight 128-key chunks; chunk c =
-//      keys [J0, J0+128), J0 = N-(c+1)*128): recomputes the chunk's scores, normalises them with
-//      the row statistics and stores them in LDS skewed by row: with
+//      keys [J0, J0+128), J0 = N-(c+1)*128): recomputes the chunk's scores,
+//      normalises them with the row statistics and stores them in LDS
+//      skewed by row: with
 //      L = last_q, P[r][j] (query i_r = N-L+r) sits at column
 //      (j - J0) + L-1 - r, so that a diagonal of the score matrix (offset
 //      o = i_r - j) is one column, x = N-1-J0-o.  Columns give the chunk's
@@ -128,10 +129,10 @@ __device__ __forceinline__ void unit_mma(const VsP& p, int key0, int rl, const t
 
 // Row statistics over one key chunk for a set of up to four listed heads
 // that read the same kv head: the workgroup stages each 64-key K tile once
-// in LDS (global -> LDS copies, double-buffered) and
-// wavefront w scores it against the 64 estimate rows of the set's head w.
-// LDS rows are 16-byte chunks, chunk c of key row r stored at c ^ (r & 15),
-// so the fragment reads of 16 consecutive rows hit distinct banks.
+// in LDS (global -> LDS copies, double-buffered) and wavefront w scores it
+// against the 64 estimate rows of the set's head w.  LDS rows are 16-byte
+// chunks, chunk c of key row r stored at c ^ (r & 15), so the fragment reads
+// of 16 consecutive rows hit distinct banks.
 template <typename T, int D>
 struct KTile {
     static constexpr int kRowBytes = D * (int)sizeof(T);
