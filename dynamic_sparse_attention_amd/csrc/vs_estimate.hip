@@ -10,7 +10,7 @@
 //      bf16/fp32 MFMA scores, the K tiles staged once per set in LDS;
 //   2. rowstat_combine: merges the chunk partials of each row in a fixed
 //      order;
-//   3. scores (batch, listed head, group of eight 128-key chunks; chunk c =
+//   3. scores (batch, listed head, group of sixteen 128-key chunks; chunk c =
 //      keys [J0, J0+128), J0 = N-(c+1)*128): recomputes the chunk's scores,
 //      normalises them with the row statistics and stores them in LDS
 //      skewed by row: with
@@ -41,7 +41,7 @@ namespace {
 constexpr int kRowstatWGs = 768;
 constexpr int kChunk2 = 128;   // keys per score work item (one 32-key unit per wavefront)
 constexpr int kSpill = 63;     // slash offsets a chunk contributes below its own range
-constexpr int kChunksPerItem = 8;  // score chunks per workgroup (the Q rows are loaded once)
+constexpr int kChunksPerItem = 16;  // score chunks per workgroup (the Q rows are loaded once)
 // LDS row pitch of the skewed probability tile (floats): 191 columns used; a
 // pitch of 194 puts the column of consecutive rows on consecutive banks.
 constexpr int kPitch2 = 194;
