@@ -12,10 +12,12 @@
 //      the row's global histogram with one atomic per non-empty bin, after
 //      finding the digit of the previous pass from that pass's complete
 //      histogram (every workgroup finds the same digit; segment 0 records it);
-//   4. with the k-th key T known, each segment counts its keys > T and == T;
-//   5. each segment writes its selected indices at the offset given by the
-//      counts of the segments before it: all keys > T, and keys == T while the
-//      row's first `need` of them (in index order) are not exhausted.
+//   4. with the k-th key T known, each wavefront counts the keys > T and == T
+//      of its contiguous slice of the segment;
+//   5. each wavefront writes the selected indices of its slice at the offset
+//      given by the counts of the slices before it: all keys > T, and keys
+//      == T while the row's first `need` of them (in index order) are not
+//      exhausted.
 // Histogram sums are integer atomics, whose totals do not depend on order.
 #include "mi_internal.h"
 #include "mi_select.h"
@@ -28,9 +30,11 @@ constexpr int kNW = kNT / 64;
 constexpr int kMaxSeg = 64;  // segments per row
 
 // Per-row scratch (uint32 words): three histograms, the state after each
-// pass (prefix, remaining rank) and the per-segment (gt, eq) counts.
+// pass (prefix, remaining rank) and the (gt, eq) counts of every wavefront
+// slice of every segment.
 constexpr int kHistWords = 2048 + 2048 + 1024;
-constexpr int kRowWords = kHistWords + 8 + 2 * kMaxSeg;
+constexpr int kRowWords = kHistWords + 8 + 2 * kMaxSeg * kNW;
+constexpr int kBatch = 16;  // keys per lane loaded together by the count and write sweeps
 
 struct TopkP {
     TopkRows t;
@@ -117,6 +121,14 @@ __global__ void __launch_bounds__(kNT) topk_hist(TopkP p, int pass) {
     const RowView v = row_view(p, row);
     if (v.k >= v.n) return;  // everything is selected
     uint32_t* st = v.scr + kHistWords;  // state: [pass] = (prefix, rem)
+    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
+    // the first keys are in flight while the previous digit is found
+    uint32_t kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = i0 + (int)threadIdx.x + u * kNT;
+        kk[u] = i < i1 ? key_of(v, i) : 0u;
+    }
     uint32_t prefix = 0, pmask = 0;
     int rem = v.k;
     if (pass > 0) {
@@ -142,13 +154,13 @@ __global__ void __launch_bounds__(kNT) topk_hist(TopkP p, int pass) {
     const int nbins = pass == 2 ? 1024 : 2048;
     for (int i = threadIdx.x; i < nbins; i += kNT) sm.hist[i] = 0u;
     __syncthreads();
-    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
     for (int base = i0 + (int)threadIdx.x; base < i1; base += 8 * kNT) {
-        uint32_t kk[8];
+        if (base != i0 + (int)threadIdx.x) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = base + u * kNT;
-            kk[u] = i < i1 ? key_of(v, i) : 0u;
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + u * kNT;
+                kk[u] = i < i1 ? key_of(v, i) : 0u;
+            }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -172,44 +184,58 @@ __device__ void threshold(const RowView& v, Smem& sm, uint32_t& T, int& need) {
     need = (int)st[3] - above;
 }
 
+// Keys of wavefront slice [w0, w1) in batches of kBatch per lane: lane l of
+// batch b holds key w0 + 64 (kBatch b + u) + l in kk[u] (0 past w1).
+__device__ __forceinline__ void load_batch(const RowView& v, int base, int w1, uint32_t (&kk)[kBatch]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int i = base + 64 * u + lane;
+        kk[u] = i < w1 ? key_of(v, i) : 0u;
+    }
+}
+
+// Each wavefront counts, over its contiguous slice of the segment (the
+// slices topk_write walks), the keys > T and == T.
 __global__ void __launch_bounds__(kNT) topk_count(TopkP p) {
     __shared__ Smem sm;
     const int row = blockIdx.x / p.nseg, s = blockIdx.x % p.nseg;
     const RowView v = row_view(p, row);
     if (v.k >= v.n) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
+    const int wseg = p.seg / kNW;
+    const int w0 = i0 + wave * wseg, w1 = min(i1, w0 + wseg);
+    // the first batch of keys is in flight while the threshold is found
+    uint32_t kk[kBatch];
+    load_batch(v, w0, w1, kk);
     uint32_t T;
     int need;
     threshold(v, sm, T, need);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
     int gt = 0, eq = 0;
-    for (int base = i0 + wave * 64; base < i1; base += kNT) {
-        const int i = base + lane;
-        const uint32_t kk = i < i1 ? key_of(v, i) : 0u;
-        gt += __popcll(__ballot(i < i1 && kk > T));
-        eq += __popcll(__ballot(i < i1 && kk == T));
-    }
-    __shared__ int32_t wc[kNW][2];
-    if (lane == 0) {
-        wc[wave][0] = gt;
-        wc[wave][1] = eq;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int g = 0, e = 0;
-        for (int w = 0; w < kNW; ++w) {
-            g += wc[w][0];
-            e += wc[w][1];
+    for (int base = w0; base < w1; base += 64 * kBatch) {
+        if (base != w0) load_batch(v, base, w1, kk);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const bool in = base + 64 * u + lane < w1;
+            gt += (in && kk[u] > T) ? 1 : 0;
+            eq += (in && kk[u] == T) ? 1 : 0;
         }
-        uint32_t* seg = v.scr + kHistWords + 8;
-        seg[2 * s] = (uint32_t)g;
-        seg[2 * s + 1] = (uint32_t)e;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        gt += __shfl_xor(gt, off, 64);
+        eq += __shfl_xor(eq, off, 64);
+    }
+    if (lane == 0) {
+        uint32_t* wcnt = v.scr + kHistWords + 8 + 2 * (s * kNW + wave);
+        wcnt[0] = (uint32_t)gt;
+        wcnt[1] = (uint32_t)eq;
     }
 }
 
 __global__ void __launch_bounds__(kNT) topk_write(TopkP p) {
     __shared__ Smem sm;
-    __shared__ int32_t wc[kNW][2];
     const int row = blockIdx.x / p.nseg, s = blockIdx.x % p.nseg;
     const RowView v = row_view(p, row);
     if (v.k >= v.n) {
@@ -218,53 +244,49 @@ __global__ void __launch_bounds__(kNT) topk_write(TopkP p) {
             for (int i = threadIdx.x; i < v.budget; i += kNT) v.out[i] = i < v.n ? i : -1;
         return;
     }
-    uint32_t T;
-    int need;
-    threshold(v, sm, T, need);
-    const uint32_t* seg = v.scr + kHistWords + 8;
-    // selected entries and keys == T in the segments before this one
-    int sel_base = 0, eq_before = 0;
-    for (int q = 0; q < s; ++q) {
-        const int e = (int)seg[2 * q + 1];
-        sel_base += (int)seg[2 * q] + min(max(need - eq_before, 0), e);
-        eq_before += e;
-    }
-    // split the segment over the wavefronts: counts first, then ordered writes
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
     const int wseg = p.seg / kNW;
     const int w0 = i0 + wave * wseg, w1 = min(i1, w0 + wseg);
-    int gt = 0, eq = 0;
-    for (int base = w0; base < w1; base += 64) {
-        const int i = base + lane;
-        const uint32_t kk = i < w1 ? key_of(v, i) : 0u;
-        gt += __popcll(__ballot(i < w1 && kk > T));
-        eq += __popcll(__ballot(i < w1 && kk == T));
+    // the first batch of keys is in flight while the threshold is found
+    uint32_t kk[kBatch];
+    load_batch(v, w0, w1, kk);
+    uint32_t T;
+    int need;
+    threshold(v, sm, T, need);
+    // selected entries and keys == T in the wavefront slices before this one
+    // (slices are ordered by key index: segment-major, then wavefront)
+    const uint32_t* wcnt = v.scr + kHistWords + 8;
+    const int before = s * kNW + wave;
+    int sel_base = 0, eq_before = 0;
+    for (int q = lane; q < before; q += 64) {
+        sel_base += (int)wcnt[2 * q];
+        eq_before += (int)wcnt[2 * q + 1];
     }
-    if (lane == 0) {
-        wc[wave][0] = gt;
-        wc[wave][1] = eq;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sel_base += __shfl_xor(sel_base, off, 64);
+        eq_before += __shfl_xor(eq_before, off, 64);
     }
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) {
-        const int e = wc[w][1];
-        sel_base += wc[w][0] + min(max(need - eq_before, 0), e);
-        eq_before += e;
-    }
-    const int eq_take = min(max(need - eq_before, 0), eq);
+    // keys == T are taken in index order until `need` are selected
+    sel_base += min(eq_before, need);
+    const int eq_left = max(need - eq_before, 0);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int run_eq = 0, run_sel = 0;
-    for (int base = w0; base < w1; base += 64) {
-        const int i = base + lane;
-        const uint32_t kk = i < w1 ? key_of(v, i) : 0u;
-        const bool g = i < w1 && kk > T;
-        const bool e = i < w1 && kk == T;
-        const uint64_t me = __ballot(e);
-        const bool sel = g || (e && run_eq + __popcll(me & below) < eq_take);
-        const uint64_t ms = __ballot(sel);
-        if (sel) v.out[sel_base + run_sel + __popcll(ms & below)] = i;
-        run_eq += __popcll(me);
-        run_sel += __popcll(ms);
+    for (int base = w0; base < w1; base += 64 * kBatch) {
+        if (base != w0) load_batch(v, base, w1, kk);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + 64 * u + lane;
+            const bool g = i < w1 && kk[u] > T;
+            const bool e = i < w1 && kk[u] == T;
+            const uint64_t me = __ballot(e);
+            const bool sel = g || (e && run_eq + __popcll(me & below) < eq_left);
+            const uint64_t ms = __ballot(sel);
+            if (sel) v.out[sel_base + run_sel + __popcll(ms & below)] = i;
+            run_eq += __popcll(me);
+            run_sel += __popcll(ms);
+        }
     }
     if (s == 0)
         for (int i = v.k + threadIdx.x; i < v.budget; i += kNT) v.out[i] = -1;
