@@ -177,6 +177,131 @@ __global__ void __launch_bounds__(kSelNT) bs_select(BsP p) {
     if (threadIdx.x == 0) p.block_count[((int64_t)b * p.Hq + h) * p.nb + a] = k;
 }
 
+// The same step with one wavefront per query block (rows of at most 64 R
+// blocks): the row lives in registers (block c = lane + 64 u in slot u), the
+// max and sum are butterfly reductions, and the selection is a 4-pass radix
+// select over 8-bit digits with a 256-bin LDS histogram per wavefront, then
+// one ordered ballot pass (slots in index order).  No workgroup barriers.
+constexpr int kWaveRows = 4;  // wavefronts (rows) per workgroup
+
+template <int R>
+__global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
+    __shared__ uint32_t hist[kWaveRows][256];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t rowid = (int64_t)blockIdx.x * kWaveRows + wv;
+    if (rowid >= (int64_t)p.B * p.n_heads * p.nb) return;
+    const int a = (int)(rowid % p.nb);
+    const int bl = (int)(rowid / p.nb);
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li];
+    float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? h : li) * p.w_h + (int64_t)a * p.nb;
+    const int n = a + 1;
+    float x[R];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        x[u] = c < n ? W[c] : -INFINITY;
+        mx = fmaxf(mx, x[u]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        x[u] = c < n ? fast_exp2((x[u] - mx) * kLog2e) : 0.f;
+        sum += x[u];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    uint32_t key[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        const float wv = c < n ? x[u] / sum : 0.f;
+        if (c < p.nb) W[c] = wv;
+        key[u] = c >= n ? 0u : ((c == 0 || c == a) ? kForcedKey : order_key(wv));
+    }
+    const int k = min(p.top, n);
+    int32_t* out = p.block_idx + (((int64_t)b * p.Hq + h) * p.nb + a) * p.top;
+    if (lane == 0) p.block_count[((int64_t)b * p.Hq + h) * p.nb + a] = k;
+    for (int m = k + lane; m < p.top; m += 64) out[m] = -1;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (k == n) {
+        // every causal block is kept
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = lane + 64 * u;
+            if (c < n) out[c] = c;
+        }
+        return;
+    }
+    // radix select: the k-th largest key T and how many keys == T to take
+    uint32_t* hw = hist[wv];
+    uint32_t prefix = 0, pmask = 0;
+    int rem = k;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = lane + 64 * u;
+            if (c < n && (key[u] & pmask) == prefix) atomicAdd(&hw[(key[u] >> shift) & 255u], 1u);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane l owns bins 255-4l .. 252-4l (descending); suffix counts from the top
+        int cnt[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cnt[i] = (int)hw[255 - 4 * lane - i];
+            local += cnt[i];
+        }
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        int run = incl - local;  // keys in higher bins than this lane's first
+        int found = -1, above = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (found < 0 && run < rem && run + cnt[i] >= rem) {
+                found = 255 - 4 * lane - i;
+                above = run;
+            }
+            run += cnt[i];
+        }
+        const uint64_t hit = __ballot(found >= 0);
+        const int src = __ffsll((long long)hit) - 1;  // exactly one lane finds the bin
+        const int digit = __shfl(found, src, 64);
+        rem -= __shfl(above, src, 64);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 255u << shift;
+        __builtin_amdgcn_wave_barrier();
+    }
+    const uint32_t T = prefix;
+    const int need = rem;
+    // ordered output: keys > T, then keys == T while fewer than `need` taken
+    int run_eq = 0, run_sel = 0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        const bool g = c < n && key[u] > T;
+        const bool e = c < n && key[u] == T;
+        const uint64_t me = __ballot(e);
+        const bool sel = g || (e && run_eq + __popcll(me & below) < need);
+        const uint64_t ms = __ballot(sel);
+        if (sel) out[run_sel + __popcll(ms & below)] = c;
+        run_eq += __popcll(me);
+        run_sel += __popcll(ms);
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -242,13 +367,28 @@ hipError_t launch_block_estimate(const BsArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bs_scores, dim3(a.B * a.n_heads * (T * (T + 1) / 2)), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t dyn = (size_t)p.nb * sizeof(float);
-    if (dyn > 48 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_select),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (e != hipSuccess) return e;
+    const int64_t sel_rows = (int64_t)a.B * a.n_heads * p.nb;
+    const dim3 wgrid((unsigned)((sel_rows + kWaveRows - 1) / kWaveRows)), wblock(64 * kWaveRows);
+    if (p.nb <= 128) {
+        hipLaunchKernelGGL(bs_select_wave<2>, wgrid, wblock, 0, s, p);
+    } else if (p.nb <= 512) {
+        hipLaunchKernelGGL(bs_select_wave<8>, wgrid, wblock, 0, s, p);
+    } else if (p.nb <= 1024) {
+        hipLaunchKernelGGL(bs_select_wave<16>, wgrid, wblock, 0, s, p);
+    } else if (p.nb <= 2048) {
+        hipLaunchKernelGGL(bs_select_wave<32>, wgrid, wblock, 0, s, p);
+    } else if (p.nb <= 4096) {
+        hipLaunchKernelGGL(bs_select_wave<64>, wgrid, wblock, 0, s, p);
+    } else {
+        // longer rows: one workgroup per row, the row staged in LDS
+        const size_t dyn = (size_t)p.nb * sizeof(float);
+        if (dyn > 48 * 1024) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_select),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(bs_select, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
     }
-    hipLaunchKernelGGL(bs_select, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
     return hipGetLastError();
 }
 
