@@ -224,6 +224,27 @@ def test_block_estimate(dtype, d, n, top):
                             f"blocks h{h} a{a}")
 
 
+@pytest.mark.parametrize("nb", [700, 1500, 4200])
+def test_block_estimate_long_rows(nb):
+    """Rows of 513-1024 and 1025-2048 blocks (16 and 32 register slots per
+    lane in the one-wavefront-per-row select) and above 4096 blocks (the
+    workgroup-per-row select)."""
+    say(f"block_estimate long rows nb={nb}")
+    n, d, top = 64 * nb, 64, 20
+    _, (q, k, _), (q64, k64, _) = _inputs(14, 1, 1, n, d, "bf16")
+    bidx, bcnt, w = mi.block_estimate(q, k, [0], top)
+    torch.cuda.synchronize()
+    bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    rw, _ = O.bs_estimate(q64[0, 0], k64[0, 0], d ** -0.5, top)
+    tri = np.tril(np.ones((nb, nb), bool))
+    assert_scores_close(w[0, 0][tri], rw[tri], "block weights")
+    assert not w[0, 0][~tri].any()
+    for a in list(range(0, nb, 37)) + [nb - 1]:
+        kk = min(top, a + 1)
+        assert bcnt[0, 0, a] == kk
+        check_selection(bidx[0, 0, a], w[0, 0, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks a{a}")
+
+
 # ----------------------------------------------------------------- index building
 
 @pytest.mark.parametrize("n,nv,ns", [(64 * 23, 40, 60), (64 * 8, 600, 600), (64 * 40, 5, 1)])
