@@ -267,10 +267,12 @@ def build_index(q, k, head_pattern: Sequence[int], vertical_idx=None, slash_idx=
 
 def sparse_prefill(q, k, v, head_pattern: Optional[Sequence[int]], index: Optional[Index],
                    sink: int = 128, local: int = 4096, scale: Optional[float] = None, out=None,
-                   lse=None, return_lse: bool = True, stream=None, schedule: bool = False):
+                   lse=None, return_lse: bool = True, stream=None, schedule: bool = False,
+                   workspace: Optional[torch.Tensor] = None):
     """Sparse attention per head pattern; head_pattern=None runs dense causal
-    attention on every head.  schedule=True passes a workspace for the item
-    schedule (grouping the heads of a kv group by pattern class).  Returns
+    attention on every head.  schedule=True (or a uint8 `workspace` tensor)
+    passes a workspace in which the library builds the item schedule
+    (grouping the heads of a kv group by pattern class).  Returns
     (o, lse | None)."""
     B, Hq, N, d = q.shape
     if out is None:
@@ -280,13 +282,31 @@ def sparse_prefill(q, k, v, head_pattern: Optional[Sequence[int]], index: Option
     desc = make_desc(q, k, v, out, scale=scale)
     pat = None if head_pattern is None else (ctypes.c_int32 * Hq)(*[int(p) for p in head_pattern])
     st = index.c_struct() if index is not None else None
-    ws = _workspace(workspace_bytes(desc, OP_SPARSE_PREFILL), q.device) if schedule else None
+    ws = workspace
+    if ws is None and schedule:
+        ws = _workspace(workspace_bytes(desc, OP_SPARSE_PREFILL), q.device)
     _check(lib().mi_sparse_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                    None if pat is None else ctypes.cast(pat, _P),
                                    None if st is None else ctypes.byref(st), sink, local,
                                    _ptr(out), _ptr(lse), None if ws is None else _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
+
+
+def attn_schedule(q, k, head_pattern: Optional[Sequence[int]], sink: int = 128, local: int = 4096,
+                  block_cap: int = 1):
+    """The attention item schedule for these shapes and patterns, built on the
+    host (mi_attn_schedule): a list of packed items, -1 for padding."""
+    desc = make_desc(q, k)
+    Hq = q.shape[1]
+    pat = None if head_pattern is None else (ctypes.c_int32 * Hq)(*[int(p) for p in head_pattern])
+    cpat = None if pat is None else ctypes.cast(pat, _P)
+    n = lib().mi_attn_schedule(ctypes.byref(desc), cpat, sink, local, block_cap, None, 0)
+    if n < 0:
+        raise MiError(7, "mi_attn_schedule rejected its arguments")
+    buf = (ctypes.c_int32 * max(n, 1))()
+    lib().mi_attn_schedule(ctypes.byref(desc), cpat, sink, local, block_cap, ctypes.cast(buf, _P), n)
+    return list(buf[:n])
 
 
 def layer_prefill(q, k, v, head_pattern: Sequence[int], *, last_q=64, n_vertical=1000, n_slash=6096,

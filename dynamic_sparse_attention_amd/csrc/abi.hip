@@ -304,14 +304,15 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
                     mi::kAttnMaxLds);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (ws) {
-        // the item schedule: copied into ws on the stream, read by the kernel
-        const std::vector<int32_t>& sched = mi::attn_schedule(a);
-        const size_t bytes = sched.size() * sizeof(int32_t);
+        // the item schedule: built into ws by a kernel on the stream, read by
+        // the attention kernel
+        const size_t bytes = (size_t)mi::attn_schedule_len(a) * sizeof(int32_t);
         if (ws_bytes < bytes) return fail(MI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, bytes);
-        if (hipMemcpyAsync(ws, sched.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-            return fail(MI_ERR_LAUNCH, "schedule upload failed: %s", hipGetErrorString(hipGetLastError()));
+        if (!aligned16(ws)) return fail(MI_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        mi_status st2 = launched(mi::launch_attn_schedule(a, static_cast<int32_t*>(ws), s));
+        if (st2 != MI_OK) return st2;
         a.sched = static_cast<const int32_t*>(ws);
-        a.sched_len = (int32_t)sched.size();
+        a.sched_len = mi::attn_schedule_len(a);
     }
     return launched(mi::launch_sparse_attn(a, s));
 }
@@ -325,7 +326,7 @@ int32_t mi_attn_schedule(const mi_attn_desc* d, const int32_t* head_pattern, int
     a.sink = sink_tokens; a.local = local_tokens; a.block_cap = block_cap;
     a.all_dense = head_pattern ? 0 : 1;
     for (int h = 0; h < d->heads_q; ++h) a.pattern[h] = head_pattern ? (uint8_t)head_pattern[h] : (uint8_t)MI_DENSE;
-    const std::vector<int32_t>& sched = mi::attn_schedule(a);
+    const std::vector<int32_t> sched = mi::attn_schedule_host(a);
     if (out)
         for (int32_t i = 0; i < cap && i < (int32_t)sched.size(); ++i) out[i] = sched[i];
     return (int32_t)sched.size();

@@ -32,11 +32,13 @@ struct AttnArgs {
     int32_t sched_len;     // entries (a multiple of 4)
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
-// Item schedule of the attention kernel (schedule.hip): bytes an upper bound
-// for any pattern set; the schedule itself is cached on the host for the life
-// of the process.
+// Item schedule of the attention kernel (schedule.hip): bytes (an upper
+// bound for any pattern set), entries for these arguments, the device build
+// into `out` (enqueued on the stream), and the same order built on the host.
 size_t attn_schedule_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N);
-const std::vector<int32_t>& attn_schedule(const AttnArgs& a);
+int32_t attn_schedule_len(const AttnArgs& a);
+hipError_t launch_attn_schedule(const AttnArgs& a, int32_t* out, hipStream_t s);
+std::vector<int32_t> attn_schedule_host(const AttnArgs& a);
 // LDS of one attention workgroup: four K/V staging tiles, the four column
 // lists of a run of query blocks and its step list (grows with seq_len and
 // col_cap).

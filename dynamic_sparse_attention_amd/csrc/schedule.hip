@@ -1,4 +1,4 @@
-// Host-side work schedule of the attention kernel.
+// Work schedule of the attention kernel.
 //
 // A work item is (batch, query head, run of four query blocks).  The kernel's
 // default order is run-major with the query heads of one kv group as four
@@ -9,17 +9,26 @@
 // head its own blocks.  Mixed groups then fetch most tiles once per head.
 //
 // The schedule groups items by (batch, kv group, pattern class) instead:
-// within a class, items are listed run-major (longest first) and cut into
-// chunks of four, so a chunk holds heads of one class of one kv group,
-// extended over consecutive runs when the group has fewer than four such
-// heads (consecutive runs of a head walk nearly the same key blocks).
-// Chunks are then ordered by estimated length, longest first.  Entries are
-// packed items ((b * Hq + h) * nruns + run); chunks shorter than four are
-// padded with -1.
+// within a sequence (b, g, class), items are listed run-major (longest
+// first) over the class's heads of the group and cut into chunks of four, so
+// a chunk holds heads of one class of one kv group, extended over
+// consecutive runs when the group has fewer than four such heads
+// (consecutive runs of a head walk nearly the same key blocks).  Chunks are
+// then ordered by estimated length, longest first, ties in sequence order.
+// Entries are packed items ((b * Hq + h) * nruns + run); chunks shorter than
+// four are padded with -1.
+//
+// The schedule is built on the device, by one thread per chunk, into the
+// caller's workspace just before the attention launch: no host memory is
+// involved, nothing is cached between calls.  A chunk's estimate is a
+// non-increasing function of its position in its sequence, so the ordered
+// position of chunk c of sequence s with estimate e is
+//     #{chunks with estimate > e}
+//   + #{chunks with estimate == e in sequences before s}
+//   + #{chunks of s before c with estimate == e},
+// each term a binary search per sequence.  mi_attn_schedule() returns the
+// same order built on the host by a plain stable sort.
 #include <algorithm>
-#include <map>
-#include <mutex>
-#include <tuple>
 #include <vector>
 
 #include "mi_internal.h"
@@ -29,32 +38,31 @@ namespace {
 
 constexpr int kRunBlocks = 4;  // query blocks per work item
 constexpr int kChunk = 4;      // items per chunk (one XCD)
+constexpr int kSchedThreads = 256;
 
-struct Key {
-    int B, Hq, Hkv, nb, all_dense, sink, local, block_cap;
-    std::vector<int> pat;
-    bool operator<(const Key& o) const {
-        return std::tie(B, Hq, Hkv, nb, all_dense, sink, local, block_cap, pat) <
-               std::tie(o.B, o.Hq, o.Hkv, o.nb, o.all_dense, o.sink, o.local, o.block_cap, o.pat);
-    }
-};
-
-int pattern_class(int p) {
+__host__ __device__ inline int pattern_class(int p) {
     if (p == MI_ASHAPE) return 1;
     if (p == MI_BSPARSE) return 2;
     return 0;  // Vertical-Slash and dense walk (nearly) every causal key block
 }
 
+struct SchedShape {
+    int32_t B, Hq, Hkv, nb, nruns, all_dense, sink, local, block_cap;
+};
+
 // Key blocks an item of this class is expected to visit.
-long estimate(int cls, int run, const Key& k) {
-    const long span = std::min(k.nb, (run + 1) * kRunBlocks);
-    if (cls == 1) return std::min<long>(span, (k.sink + 63) / 64 + (k.local + 126) / 64 + kRunBlocks);
-    if (cls == 2) return std::min<long>(span, (long)kRunBlocks * k.block_cap);
-    return span;
+__host__ __device__ inline long estimate(int cls, int run, const SchedShape& k) {
+    const long full = (long)(run + 1) * kRunBlocks;
+    const long span = full < k.nb ? full : (long)k.nb;
+    long cap = span;
+    if (cls == 1) cap = (long)((k.sink + 63) / 64 + (k.local + 126) / 64 + kRunBlocks);
+    if (cls == 2) cap = (long)kRunBlocks * k.block_cap;
+    return span < cap ? span : cap;
 }
 
-std::vector<int32_t> build(const Key& k) {
-    const int nruns = (k.nb + kRunBlocks - 1) / kRunBlocks;
+// ---------------------------------------------------------------- host
+
+std::vector<int32_t> build_host(const SchedShape& k, const uint8_t* pat) {
     const int group = k.Hq / k.Hkv;
     struct Chunk {
         long est;
@@ -67,15 +75,15 @@ std::vector<int32_t> build(const Key& k) {
             for (int cls = 0; cls < 3; ++cls) {
                 heads.clear();
                 for (int h = g * group; h < (g + 1) * group; ++h)
-                    if (pattern_class(k.all_dense ? MI_DENSE : k.pat[h]) == cls) heads.push_back(h);
+                    if (pattern_class(k.all_dense ? MI_DENSE : pat[h]) == cls) heads.push_back(h);
                 if (heads.empty()) continue;
                 Chunk c{};
                 int fill = 0;
-                for (int pos = 0; pos < nruns; ++pos) {
-                    const int run = nruns - 1 - pos;
+                for (int pos = 0; pos < k.nruns; ++pos) {
+                    const int run = k.nruns - 1 - pos;
                     for (int h : heads) {
                         if (fill == 0) c.est = estimate(cls, run, k);
-                        c.it[fill++] = (int32_t)(((int64_t)b * k.Hq + h) * nruns + run);
+                        c.it[fill++] = (int32_t)(((int64_t)b * k.Hq + h) * k.nruns + run);
                         if (fill == kChunk) {
                             chunks.push_back(c);
                             fill = 0;
@@ -94,6 +102,111 @@ std::vector<int32_t> build(const Key& k) {
     return out;
 }
 
+// ---------------------------------------------------------------- device
+
+struct SchedParams {
+    SchedShape k;
+    int32_t per_batch;  // chunks of one batch entry
+    int32_t* out;
+    uint8_t pattern[MI_MAX_HEADS];
+};
+
+// Sequence (g, class) of one batch entry: its heads and chunk count.
+struct Seq {
+    int nh, nchunks;
+};
+
+__device__ inline Seq seq_of(const SchedParams& p, int g, int cls, int group) {
+    int nh = 0;
+    for (int h = g * group; h < (g + 1) * group; ++h)
+        nh += pattern_class(p.k.all_dense ? MI_DENSE : p.pattern[h]) == cls;
+    return Seq{nh, (p.k.nruns * nh + kChunk - 1) / kChunk};
+}
+
+// Estimate of chunk c of a sequence with nh heads (from its first item).
+__device__ inline long chunk_est(const SchedParams& p, int cls, int nh, int c) {
+    const int run = p.k.nruns - 1 - (kChunk * c) / nh;
+    return estimate(cls, run, p.k);
+}
+
+// First chunk of the sequence whose estimate is <= e (strict = false: < e).
+__device__ inline int first_below(const SchedParams& p, int cls, const Seq& s, long e, bool strict) {
+    int lo = 0, hi = s.nchunks;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const long v = chunk_est(p, cls, s.nh, mid);
+        if (strict ? v < e : v <= e) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+__global__ void __launch_bounds__(kSchedThreads) attn_schedule_kernel(SchedParams p) {
+    const int64_t t = (int64_t)blockIdx.x * kSchedThreads + threadIdx.x;
+    const int64_t total = (int64_t)p.k.B * p.per_batch;
+    if (t >= total) return;
+    const int group = p.k.Hq / p.k.Hkv;
+    const int b = (int)(t / p.per_batch);
+    int r = (int)(t % p.per_batch);
+    // locate the thread's sequence (g, cls) and chunk c
+    int g = 0, cls = 0;
+    Seq s{0, 0};
+    for (int q = 0; q < 3 * p.k.Hkv; ++q) {
+        s = seq_of(p, q / 3, q % 3, group);
+        if (r < s.nchunks) {
+            g = q / 3;
+            cls = q % 3;
+            break;
+        }
+        r -= s.nchunks;
+    }
+    const int c = r;
+    const long e = chunk_est(p, cls, s.nh, c);
+    // ordered position
+    int64_t gt = 0, eq_before = 0;
+    const int me = 3 * g + cls;
+    for (int q = 0; q < 3 * p.k.Hkv; ++q) {
+        const int cq = q % 3;
+        const Seq sq = seq_of(p, q / 3, cq, group);
+        if (sq.nchunks == 0) continue;
+        const int n_gt = first_below(p, cq, sq, e, false);  // chunks with estimate > e
+        const int n_ge = first_below(p, cq, sq, e, true);   // chunks with estimate >= e
+        gt += n_gt;
+        eq_before += (int64_t)(n_ge - n_gt) * b + (q < me ? n_ge - n_gt : 0);
+        if (q == me) eq_before += c - n_gt;
+    }
+    const int64_t rank = gt * p.k.B + eq_before;
+    if (rank < 0 || rank >= total) return;  // unreachable: ranks are a permutation of the chunks
+    int32_t* dst = p.out + rank * kChunk;
+    const int g_heads = s.nh;
+    const int64_t len = (int64_t)p.k.nruns * g_heads;
+    for (int j = 0; j < kChunk; ++j) {
+        const int64_t i = (int64_t)kChunk * c + j;
+        int32_t item = -1;
+        if (i < len) {
+            const int pos = (int)(i / g_heads), hk = (int)(i % g_heads);
+            // the hk-th head of class cls in group g
+            int h = g * group, seen = -1;
+            for (; h < (g + 1) * group; ++h) {
+                seen += pattern_class(p.k.all_dense ? MI_DENSE : p.pattern[h]) == cls;
+                if (seen == hk) break;
+            }
+            const int run = p.k.nruns - 1 - pos;
+            item = (int32_t)(((int64_t)b * p.k.Hq + h) * p.k.nruns + run);
+        }
+        dst[j] = item;
+    }
+}
+
+SchedShape shape_of(const AttnArgs& a) {
+    SchedShape k{};
+    k.B = a.B; k.Hq = a.Hq; k.Hkv = a.Hkv; k.nb = a.N / 64;
+    k.nruns = (k.nb + kRunBlocks - 1) / kRunBlocks;
+    k.all_dense = a.all_dense; k.sink = a.sink; k.local = a.local;
+    k.block_cap = std::max(a.block_cap, 1);
+    return k;
+}
+
 }  // namespace
 
 size_t attn_schedule_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N) {
@@ -102,18 +215,33 @@ size_t attn_schedule_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N) {
     return ((size_t)B * Hq * nruns + (size_t)B * Hkv * 3 * (kChunk - 1)) * sizeof(int32_t);
 }
 
-// The schedule for these arguments.  Schedules are kept for the life of the
-// process (one per distinct layer shape and pattern set), so the host memory
-// an asynchronous copy reads stays valid.
-const std::vector<int32_t>& attn_schedule(const AttnArgs& a) {
-    static std::mutex mu;
-    static std::map<Key, std::vector<int32_t>> cache;
-    Key k{a.B, a.Hq, a.Hkv, a.N / 64, a.all_dense, a.sink, a.local, std::max(a.block_cap, 1), {}};
-    k.pat.assign(a.pattern, a.pattern + a.Hq);
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(k);
-    if (it == cache.end()) it = cache.emplace(k, build(k)).first;
-    return it->second;
+int32_t attn_schedule_len(const AttnArgs& a) {
+    const SchedShape k = shape_of(a);
+    const int group = k.Hq / k.Hkv;
+    int64_t per_batch = 0;
+    for (int g = 0; g < k.Hkv; ++g)
+        for (int cls = 0; cls < 3; ++cls) {
+            int nh = 0;
+            for (int h = g * group; h < (g + 1) * group; ++h)
+                nh += pattern_class(k.all_dense ? MI_DENSE : a.pattern[h]) == cls;
+            per_batch += (k.nruns * (int64_t)nh + kChunk - 1) / kChunk;
+        }
+    return (int32_t)(per_batch * k.B * kChunk);
+}
+
+std::vector<int32_t> attn_schedule_host(const AttnArgs& a) { return build_host(shape_of(a), a.pattern); }
+
+hipError_t launch_attn_schedule(const AttnArgs& a, int32_t* out, hipStream_t s) {
+    SchedParams p{};
+    p.k = shape_of(a);
+    p.per_batch = attn_schedule_len(a) / (kChunk * p.k.B);
+    p.out = out;
+    for (int h = 0; h < MI_MAX_HEADS; ++h) p.pattern[h] = a.pattern[h];
+    const int64_t total = (int64_t)p.k.B * p.per_batch;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3((unsigned)((total + kSchedThreads - 1) / kSchedThreads)),
+                       dim3(kSchedThreads), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace mi

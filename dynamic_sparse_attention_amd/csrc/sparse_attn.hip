@@ -154,7 +154,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <typename T, int D>
 __device__ __forceinline__ void issue_rows(char* dst, uint32_t w, const int32_t* tok_src, int32_t* tok_dst,
                                            const char* base, int64_t stride_b, int rank, int it0, int it1) {
-    const int lane = threadIdx.x & 63;
+    int lane = threadIdx.x & 63;
+    // fp32 rows of 128 elements: eight copy instructions per wavefront; an
+    // opaque lane id keeps their addresses from being hoisted out of the
+    // step loop (they would not fit in registers and would spill)
+    if constexpr (sizeof(T) == 4 && D == 128) asm volatile("" : "+v"(lane));
     const bool col = step_col(w);
     const char* tile = base + (int64_t)step_kb(w) * 64 * stride_b;
 #pragma unroll
@@ -386,18 +390,52 @@ __device__ __forceinline__ int step_mode(uint32_t w, const Params& p, int patter
     return kb >= my_a ? kMaskCausal : kMaskNone;
 }
 
+// The wavefront's Q^T operand (32 rows x D).  Held in registers, except
+// for fp32 rows of 128 elements, whose 64 registers would not fit beside the
+// accumulators at two wavefronts per SIMD: those fragments are re-read from
+// global memory (the 16 KiB of a wavefront's rows stay in the L1/L2 caches)
+// at each use.
+template <typename T, int D>
+struct QOperand {
+    typedef typename Elem<T>::frag Frag;
+    static constexpr bool kRegs = !(sizeof(T) == 4 && D == 128);
+    Frag f[kRegs ? D / 16 : 1];
+    const T* row;  // this lane's row, offset by its contraction half (8 hl)
+    __device__ __forceinline__ void init(const T* qrow, bool active) {
+        row = qrow;
+        if constexpr (kRegs) {
+            if (active) {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) f[s] = load_frag(qrow + 16 * s);
+            } else {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) f[s] = Frag{};
+            }
+        }
+    }
+    __device__ __forceinline__ Frag get(int ks) const {
+        if constexpr (kRegs) return f[ks];
+        else return load_frag(row + 16 * ks);
+    }
+};
+
 // S^T = K . Q^T for one step (the two 32-key halves interleaved).
 template <typename T, int D>
 __device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, const LaneBase& lb,
-                                          const typename Elem<T>::frag (&qf)[D / 16]) {
+                                          const QOperand<T, D>& qf) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kh][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const typename Elem<T>::frag qk = qf.get(ks);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) mma32(s[kh], k_frag<T, D>(kbuf, lb, kh, ks), qf[ks]);
+        for (int kh = 0; kh < 2; ++kh) mma32(s[kh], k_frag<T, D>(kbuf, lb, kh, ks), qk);
+        // fp32: keep each slice's operand reads next to its MFMAs (hoisting
+        // them all would need more registers than two wavefronts per SIMD have)
+        if constexpr (sizeof(T) == 4) __builtin_amdgcn_sched_barrier(0);
+    }
     // bf16 schedule: four operand reads ahead, then one MFMA per read, so
     // that LDS latency hides behind the MFMA chain
     if constexpr (sizeof(T) == 2) {
@@ -510,8 +548,10 @@ __device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vb
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db) {
                 mma32(rs.oacc[db], v_frag<T, D>(vbuf, lb, db, kh * 32 + pp * 16), pf[kh][pp]);
+                if constexpr (sizeof(T) == 4) __builtin_amdgcn_sched_barrier(0);
+            }
     // bf16 schedule: eight transposed reads (four operands) ahead, then one
     // MFMA per operand
     if constexpr (sizeof(T) == 2) {
@@ -522,6 +562,39 @@ __device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vb
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
     }
+}
+
+// fp32: the probabilities overwrite the scores (an fp32 P operand is the
+// score registers themselves); returns their sum.
+__device__ __forceinline__ float probs_in_place(f32x16 (&s)[2], float m_use, float c) {
+    float sum = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[kh][e] = fast_exp2(fmaf(s[kh][e], c, -m_use));
+            sum += s[kh][e];
+        }
+    return sum;
+}
+
+// fp32 O^T += V^T . P^T with P read straight from the score registers
+// (16-key chunk pp of half kh is elements 8 pp .. 8 pp + 7 of s[kh]).
+template <int D>
+__device__ __forceinline__ void pv_accumulate_f32(RowState<float, D>& rs, const char* vbuf, const LaneBase& lb,
+                                                  const f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const f32x8 pf = {s[kh][8 * pp + 0], s[kh][8 * pp + 1], s[kh][8 * pp + 2], s[kh][8 * pp + 3],
+                              s[kh][8 * pp + 4], s[kh][8 * pp + 5], s[kh][8 * pp + 6], s[kh][8 * pp + 7]};
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                mma32(rs.oacc[db], v_frag<float, D>(vbuf, lb, db, kh * 32 + pp * 16), pf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 }
 
 // Between phases a wavefront carries either its scores or its P operands,
@@ -572,7 +645,6 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     typedef typename Elem<T>::frag Frag;
     typedef Layout<T, D> Ly;
     typedef Arena<T, D> Ar;
-    constexpr int NKS = D / 16;
     constexpr int NDB = D / 32;
     __shared__ __attribute__((aligned(1024))) char kbuf0[Ly::TILEB];
     __shared__ __attribute__((aligned(1024))) char kbuf1[Ly::TILEB];
@@ -588,8 +660,9 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     if (p.sched) {
         // scheduled order: chunks of four items of one kv group and pattern
         // class, longest first
+        if (L >= p.sched_len) return;
         const int it = ld_uniform(p.sched + L);
-        if (it < 0) return;
+        if (it < 0 || it >= items) return;
         run = it % p.nruns;
         bh = it / p.nruns;
     } else {
@@ -629,15 +702,8 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
         return t < nsteps ? (uint32_t)__builtin_amdgcn_readfirstlane(steps[t]) : kNoStep;
     };
 
-    Frag qf[NKS];
-    if (active) {
-        const T* qrow = qbase + (int64_t)i_row * p.qs2;
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) qf[s] = load_frag(qrow + 16 * s + 8 * hl);
-    } else {
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) qf[s] = Frag{};
-    }
+    QOperand<T, D> qf;
+    qf.init(qbase + (int64_t)i_row * p.qs2 + 8 * hl, active);
     const LaneBase lb = lane_base<T, D>(lane);
 
     RowState<T, D> rs;
@@ -680,9 +746,13 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
 #pragma unroll
                             for (int e = 0; e < 16; ++e) rs.oacc[db][e] *= alpha;
                     }
-                    Frag pf[2][2];
-                    unpark_p(pf, s);
-                    pv_accumulate<T, D>(rs, vprev, lbo, pf);
+                    if constexpr (sizeof(T) == 2) {
+                        Frag pf[2][2];
+                        unpark_p(pf, s);
+                        pv_accumulate<T, D>(rs, vprev, lbo, pf);
+                    } else {
+                        pv_accumulate_f32<D>(rs, vprev, lbo, s);
+                    }
                 }
                 if (s_need) {
                     s_compute<T, D>(s, kcur, lbo, qf);
@@ -704,9 +774,13 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
                 if (grp == 1 ? pv_need : s_need) {
                     rescale = raise_max<T, D>(rs, row_max(s, p.c), alpha);
                     const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
-                    Frag pf[2][2];
-                    rs.l_part += probs_half<T>(pf[0], s[0], m_use, p.c) + probs_half<T>(pf[1], s[1], m_use, p.c);
-                    park_p(s, pf);
+                    if constexpr (sizeof(T) == 2) {
+                        Frag pf[2][2];
+                        rs.l_part += probs_half<T>(pf[0], s[0], m_use, p.c) + probs_half<T>(pf[1], s[1], m_use, p.c);
+                        park_p(s, pf);
+                    } else {
+                        rs.l_part += probs_in_place(s, m_use, p.c);
+                    }
                 }
             }
             if (ph == 0) phase_barrier();

@@ -95,8 +95,10 @@ typedef struct {
 
 /* Bytes of workspace an operation needs.  op = MI_OP_VS_ESTIMATE: p0 = number
  * of listed heads; MI_OP_BLOCK_ESTIMATE: p0 = number of listed heads;
- * MI_OP_SPARSE_PREFILL: the item schedule (optional: with ws = NULL the
- * kernel uses its default order).  Returns 0 for an invalid desc. */
+ * MI_OP_SPARSE_PREFILL: the attention item schedule, which mi_sparse_prefill
+ * builds in ws with a kernel on the stream before the attention reads it
+ * (optional: with ws = NULL the attention uses its default order).  Returns
+ * 0 for an invalid desc. */
 size_t mi_workspace_bytes(const mi_attn_desc* desc, int32_t op, int32_t p0, int32_t p1);
 
 /* Vertical-Slash index estimate (hotpaper.ai summary of arXiv 2407.02490, key
@@ -199,14 +201,21 @@ mi_status mi_build_index(const mi_attn_desc* desc, const int32_t* head_pattern,
  * may then be NULL).  O is written in desc->dtype; bf16 inputs use bf16 MFMA
  * with fp32 softmax and accumulation, f32 inputs use fp32 MFMA.
  *   o    [batch, heads_q, seq_len, head_dim] with desc->o_stride
- *   lse  float [batch, heads_q, seq_len] or NULL */
+ *   lse  float [batch, heads_q, seq_len] or NULL
+ *   ws   NULL, or >= mi_workspace_bytes(desc, MI_OP_SPARSE_PREFILL, 0, 0)
+ *        bytes of 16-byte aligned device memory: the call then enqueues a
+ *        small kernel that writes the item schedule of mi_attn_schedule()
+ *        into ws, and the attention runs its work items in that order (the
+ *        results are bit-identical either way).  ws is overwritten by every
+ *        call; two calls sharing it on different streams race. */
 mi_status mi_sparse_prefill(const mi_attn_desc* desc, const void* q, const void* k,
                             const void* v, const int32_t* head_pattern, const mi_index* idx,
                             int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* The attention item schedule that mi_sparse_prefill copies into its ws
- * (host call, no device work).  Items are runs of four 64-row query blocks
+/* The attention item schedule that mi_sparse_prefill builds in its ws on
+ * the device, computed here on the host (host call, no device work, no
+ * state kept between calls).  Items are runs of four 64-row query blocks
  * of one (batch, query head), packed as (b * heads_q + h) * nruns + run with
  * nruns = ceil(seq_len / 256); -1 marks padding.  Consecutive groups of four
  * entries hold items of one kv group and one pattern class (Vertical-Slash

@@ -2,13 +2,24 @@
 launch configuration the benchmark times (LayerPlan: one stream, workspace
 scores, index sized by index_caps).
 
-Estimates are compared with the oracle in full (or on sampled heads/rows
-where the fp64 oracle would take minutes); selections pass the exact gate on
-the GPU's own scores everywhere they are compared; index lists are compared
-exactly on sampled query blocks; attention rows are compared on sampled
-query blocks (rows are independent given the index), always including
-blocks 0, 1, nb/2 and nb-1.  Full-size properties (ascending lists,
-diagonal present, counts within caps) are checked on every row."""
+What is compared with the oracle, per layer:
+  * estimates: vertical / slash scores and block weights element by element
+    (1e-3 relative) for every head at the 2K, 32K and 128K layers, for
+    sampled heads at 256K and 1M; selections pass the exact gate on the GPU's
+    own scores and are compared with the fp64 selection (near ties reported);
+  * index lists: every query block of at least one head per pattern, and
+    sampled query blocks of every other head, exactly;
+  * attention rows fed the GPU's index on 16 query blocks of at least four
+    heads (rows are independent given the index), always including blocks 0,
+    1, nb/2 and nb-1;
+  * the dense comparator (no index) on sampled rows at 128K and 1M;
+  * full-size properties (ascending lists ending in the diagonal block,
+    counts within caps) on every row.
+The index comparison runs on a thread pool (the oracle's list arithmetic
+releases the GIL); attention and estimates run serially, on the BLAS threads."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -29,10 +40,27 @@ def _gpu():
     mi.lib()
 
 
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def pmap(fn, items):
+    items = list(items)
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
 def _blocks_to_check(nb, n_random, seed):
+    """Query blocks 0, 1, nb/2, nb-1 plus seeded random ones (16 in total for
+    n_random = 12 when nb is large)."""
     rng = np.random.default_rng(seed)
     fixed = {0, min(1, nb - 1), nb // 2, nb - 1}
-    rnd = set(int(x) for x in rng.choice(nb, min(n_random, nb), replace=False))
+    rest = np.setdiff1d(np.arange(nb), sorted(fixed))
+    rnd = set(int(x) for x in rng.choice(rest, min(n_random, len(rest)), replace=False))
     return sorted(fixed | rnd)
 
 
@@ -48,12 +76,22 @@ def _run_plan(w, data):
     return plan, pats
 
 
-def check_layer(w, *, vs_full_heads, bs_full_heads, bs_rows, idx_blocks, att_heads, att_blocks, seed):
+def _ashape_blocks_closed_form(a, sink, local):
+    """Key blocks of an A-shape query block: c <= a holding a sink key
+    (64c < sink) or within the window of some row (64(a-c) - 63 < local).
+    Pinned against the oracle's brute force in the CPU tests; used where the
+    brute force (64 rows of up to N keys per block) would take minutes."""
+    c = np.arange(a + 1)
+    return c[(64 * c < sink) | (64 * (a - c) - 63 < local)]
+
+
+def check_layer(w, *, est_heads, bs_all_rows_heads, bs_rows, full_index_heads, idx_blocks,
+                att_heads, att_blocks, dense_heads=(), dense_blocks=()):
     say(f"config {w.name}: generating")
     data = W.generate(w)
     plan, pats = _run_plan(w, data)
     say(f"config {w.name}: GPU layer done")
-    n, nb, g, d = w.seq_len, w.n_blocks, w.group, w.head_dim
+    n, nb, g = w.seq_len, w.n_blocks, w.group
     f64 = lambda x, h: W.to_f64(x[0, h], w.dtype)
     idx = plan.index
     bc = idx.block_count[0].cpu().numpy()
@@ -66,80 +104,144 @@ def check_layer(w, *, vs_full_heads, bs_full_heads, bs_rows, idx_blocks, att_hea
     oracle_index = {}
     vidx = plan.vidx[0].cpu().numpy() if plan.vidx is not None else None
     sidx = plan.sidx[0].cpu().numpy() if plan.sidx is not None else None
-    for li, h in enumerate(plan.vs_heads):
+    for h in plan.vs_heads:
         Vh, Sh = vidx[h][vidx[h] >= 0], sidx[h][sidx[h] >= 0]
+        assert np.all(np.diff(Vh) > 0) and np.all(np.diff(Sh) > 0) and Vh[0] == 0 and Sh[0] == 0
         oracle_index[h] = O.HeadIndex(O.VSLASH, n, V=Vh, S=Sh)
-        if h in vs_full_heads:
-            say(f"  VS head {h}: estimate")
-            # same estimate with caller score buffers: identical selections, scores visible
-            ev, es, gv, gs = mi.vs_estimate(plan.q, plan.k, [h], w.last_q, w.n_vertical, w.n_slash,
-                                            w.force_vertical, w.force_slash)
-            torch.cuda.synchronize()
-            assert np.array_equal(ev[0, h].cpu().numpy(), vidx[h])
-            assert np.array_equal(es[0, h].cpu().numpy(), sidx[h])
-            gv, gs = gv[0, h].double().cpu().numpy(), gs[0, h].double().cpu().numpy()
-            rv, rs = O.vs_estimate(f64(data["q"], h), f64(data["k"], h // g), w.scale, w.last_q)
-            assert_scores_close(gv, rv, f"vertical h{h}")
-            assert_scores_close(gs, rs, f"slash h{h}")
-            check_selection(vidx[h], gv, rv, w.n_vertical, range(w.force_vertical), f"vertical h{h}")
-            check_selection(sidx[h], gs, rs, w.n_slash, range(w.force_slash), f"slash h{h}")
+
+    # ---- Vertical-Slash estimates: one call with caller score buffers for
+    # the checked heads (identical selections), scores against the oracle
+    vs_est = [h for h in plan.vs_heads if h in est_heads]
+    if vs_est:
+        say(f"  VS estimates of {len(vs_est)} heads")
+        ev, es, gv, gs = mi.vs_estimate(plan.q, plan.k, vs_est, w.last_q, w.n_vertical, w.n_slash,
+                                        w.force_vertical, w.force_slash)
+        torch.cuda.synchronize()
+        ev, es = ev[0].cpu().numpy(), es[0].cpu().numpy()
+        gv, gs = gv[0].double().cpu().numpy(), gs[0].double().cpu().numpy()
+
+        def one(h):
+            return O.vs_estimate(f64(data["q"], h), f64(data["k"], h // g), w.scale, w.last_q)
+
+        for h, (rv, rs) in zip(vs_est, map(one, vs_est)):
+            assert np.array_equal(ev[h], vidx[h]) and np.array_equal(es[h], sidx[h]), h
+            assert_scores_close(gv[h], rv, f"vertical h{h}")
+            assert_scores_close(gs[h], rs, f"slash h{h}")
+            check_selection(vidx[h], gv[h], rv, w.n_vertical, range(w.force_vertical), f"vertical h{h}")
+            check_selection(sidx[h], gs[h], rs, w.n_slash, range(w.force_slash), f"slash h{h}")
+        del gv, gs
+
+    # ---- Block-Sparse estimates
     if plan.bs_heads:
         bidx = plan.bidx[0].cpu().numpy()
         bcnt = plan.bcnt[0].cpu().numpy()
         for h in plan.bs_heads:
-            kept = [bidx[h, a, : bcnt[h, a]] for a in range(nb)]
-            oracle_index[h] = O.HeadIndex(O.BSPARSE, n, kept=kept)
-            if h in bs_full_heads:
-                say(f"  BS head {h}: estimate")
-                rw, rkept = O.bs_estimate(f64(data["q"], h), f64(data["k"], h // g), w.scale, w.top_blocks)
-                # same estimate with a caller weight buffer: identical lists, weights visible
-                eb, ec, gw = mi.block_estimate(plan.q, plan.k, [h], w.top_blocks)
-                torch.cuda.synchronize()
-                assert np.array_equal(eb[0, h].cpu().numpy(), bidx[h])
-                assert np.array_equal(ec[0, h].cpu().numpy(), bcnt[h])
-                gw = gw[0, h].double().cpu().numpy()
-                tri = np.tril(np.ones((nb, nb), bool))
-                assert_scores_close(gw[tri], rw[tri], f"block weights h{h}")
-                for a in sorted(set(bs_rows) | {0, nb - 1}):
-                    kk = min(w.top_blocks, a + 1)
-                    check_selection(bidx[h, a], gw[a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks h{h} a{a}")
+            oracle_index[h] = O.HeadIndex(O.BSPARSE, n, kept=[bidx[h, a, : bcnt[h, a]] for a in range(nb)])
+        bs_est = [h for h in plan.bs_heads if h in est_heads]
+        tri = np.tril(np.ones((nb, nb), bool))
+        for h in bs_est:
+            say(f"  BS estimate of head {h}")
+            eb, ec, gw = mi.block_estimate(plan.q, plan.k, [h], w.top_blocks)
+            torch.cuda.synchronize()
+            assert np.array_equal(eb[0, h].cpu().numpy(), bidx[h])
+            assert np.array_equal(ec[0, h].cpu().numpy(), bcnt[h])
+            gw = gw[0, h].double().cpu().numpy()
+            rw, _ = O.bs_estimate(f64(data["q"], h), f64(data["k"], h // g), w.scale, w.top_blocks)
+            assert_scores_close(gw[tri], rw[tri], f"block weights h{h}")
+            assert not gw[~tri].any()
+            rows = range(nb) if h in bs_all_rows_heads else sorted(set(bs_rows) | {0, nb - 1})
+            for a in rows:
+                kk = min(w.top_blocks, a + 1)
+                assert bcnt[h, a] == kk
+                check_selection(bidx[h, a], gw[a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks h{h} a{a}")
+            del gw, rw
     for h, p in enumerate(pats):
         if p == W.ASHAPE:
             oracle_index[h] = O.HeadIndex(O.ASHAPE, n, sink=w.sink, local=w.local)
-    # index lists, exact, on sampled query blocks
+
+    # ---- index lists, exact
     for h in range(w.heads_q):
         ih = oracle_index[h]
-        for a in idx_blocks:
-            got_b = idx.block_idx[0, h, a, : bc[h, a]].cpu().numpy()
-            got_c = idx.col_idx[0, h, a, : cc[h, a]].cpu().numpy()
-            ref_b = ih.blocks(a)
-            assert np.array_equal(got_b, ref_b), (h, a)
-            assert np.array_equal(got_c, ih.cols(a)), (h, a)
+        full = h in full_index_heads
+        blocks_here = np.arange(nb) if full else np.asarray(idx_blocks)
+        sel = torch.from_numpy(blocks_here).cuda()
+        bi_h = idx.block_idx[0, h].index_select(0, sel).cpu().numpy()
+        ci_h = idx.col_idx[0, h].index_select(0, sel).cpu().numpy()
+
+        def check_block(r, ih=ih, bi_h=bi_h, ci_h=ci_h, h=h, full=full, blocks_here=blocks_here):
+            a = int(blocks_here[r])
+            got_b = bi_h[r, : bc[h, a]]
+            got_c = ci_h[r, : cc[h, a]]
+            if not (np.all(bi_h[r, bc[h, a]:] == -1) and np.all(ci_h[r, cc[h, a]:] == -1)):
+                return f"padding h{h} a{a}"
+            if ih.pattern == O.ASHAPE and full and a not in idx_blocks:
+                ref_b = _ashape_blocks_closed_form(a, w.sink, w.local)
+            else:
+                ref_b = ih.blocks(a)
+            if not np.array_equal(got_b, ref_b):
+                return f"block list h{h} a{a}"
+            ref_c = O.vs_column_list(a, ih.V, ref_b) if ih.pattern == O.VSLASH else np.zeros(0, np.int64)
+            if not np.array_equal(got_c, ref_c):
+                return f"column list h{h} a{a}"
+            return None
+
+        bad = [x for x in pmap(check_block, range(len(blocks_here))) if x]
+        assert not bad, bad[:5]
+        del bi_h, ci_h
+        if full:
+            say(f"  index of head {h} (pattern {pats[h]}): all {nb} query blocks match")
     say(f"config {w.name}: index lists match")
-    # attention rows fed the GPU's index
+
+    # ---- attention rows fed the GPU's index
     of = plan.o[0]
     atol = F32_ATOL if w.dtype == "f32" else BF16_ATOL
-    worst = 0.0
-    for h in att_heads:
+    items = [(h, a) for h in att_heads for a in att_blocks]
+    got_rows = {(h, a): of[h, 64 * a: 64 * a + 64].double().cpu().numpy() for h, a in items}
+
+    def att_err(item):
+        h, a = item
         qh, kh, vh = f64(data["q"], h), f64(data["k"], h // g), f64(data["v"], h // g)
-        res = O.head_attention(qh, kh, vh, w.scale, oracle_index[h], att_blocks)
-        for a, (ref, _) in res.items():
-            got = of[h, 64 * a: 64 * a + 64].double().cpu().numpy()
-            err = float(np.abs(got - ref).max())
-            worst = max(worst, err)
-            assert err < atol, (h, a, err)
+        ref, _ = O.head_attention(qh, kh, vh, w.scale, oracle_index[h], [a])[a]
+        return float(np.abs(got_rows[item] - ref).max())
+
+    errs = [att_err(it) for it in items]
+    worst = max(errs)
+    bad = [(it, e) for it, e in zip(items, errs) if not e < atol]
+    assert not bad, bad[:5]
     say(f"config {w.name}: attention max abs error {worst:.3e} over {len(att_heads)} heads x "
         f"{len(att_blocks)} blocks")
+
+    # ---- dense comparator (same kernel, no index) on sampled rows
+    if dense_heads:
+        plan.attention(dense=True)
+        torch.cuda.synchronize()
+        items = [(h, a) for h in dense_heads for a in dense_blocks]
+        got_rows = {(h, a): of[h, 64 * a: 64 * a + 64].double().cpu().numpy() for h, a in items}
+        dense_idx = O.HeadIndex(O.DENSE, n)
+
+        def dense_err(item):
+            h, a = item
+            qh, kh, vh = f64(data["q"], h), f64(data["k"], h // g), f64(data["v"], h // g)
+            ref, _ = O.head_attention(qh, kh, vh, w.scale, dense_idx, [a])[a]
+            return float(np.abs(got_rows[item] - ref).max())
+
+        errs = [dense_err(it) for it in items]
+        bad = [(it, e) for it, e in zip(items, errs) if not e < atol]
+        assert not bad, bad[:5]
+        say(f"config {w.name}: dense comparator max abs error {max(errs):.3e} over {len(items)} blocks")
     return plan, data, oracle_index
 
 
 def test_c1_vs_single_head_fp32():
     w = W.C1
-    plan, data, oidx = check_layer(w, vs_full_heads=[0], bs_full_heads=[], bs_rows=[],
+    plan, data, oidx = check_layer(w, est_heads=[0], bs_all_rows_heads=[], bs_rows=[], full_index_heads=[0],
                                    idx_blocks=range(w.n_blocks), att_heads=[0],
-                                   att_blocks=list(range(w.n_blocks)), seed=1)
-    # end to end against the oracle's own estimate and index (reported, and
-    # equal here unless a near tie flipped a selection)
+                                   att_blocks=list(range(w.n_blocks)), dense_heads=[0],
+                                   dense_blocks=list(range(w.n_blocks)))
+    # end to end against the oracle's own estimate and index (equal here
+    # unless a near tie flipped a selection)
+    plan.attention()
+    torch.cuda.synchronize()
     q64, k64, v64 = (W.to_f64(data[x][0, 0], "f32") for x in ("q", "k", "v"))
     own, _ = O.build_head_index(O.VSLASH, q64, k64, w.scale, last_q=w.last_q, n_vertical=w.n_vertical,
                                 n_slash=w.n_slash)
@@ -154,18 +256,22 @@ def test_c2_block_sparse_gqa():
     w = W.C2
     nb = w.n_blocks
     blocks = _blocks_to_check(nb, 12, 2)
-    check_layer(w, vs_full_heads=[], bs_full_heads=[0, 13, 31], bs_rows=blocks, idx_blocks=blocks,
-                att_heads=list(range(0, 32, 3)), att_blocks=blocks, seed=2)
+    check_layer(w, est_heads=range(w.heads_q), bs_all_rows_heads=range(w.heads_q), bs_rows=blocks,
+                full_index_heads=[0, 13], idx_blocks=blocks, att_heads=list(range(0, 32, 3)),
+                att_blocks=blocks)
 
 
+@pytest.mark.timeout(600)
 def test_c3_vertical_slash_128k():
     w = W.C3
     nb = w.n_blocks
-    check_layer(w, vs_full_heads=[0, 5, 17, 31], bs_full_heads=[], bs_rows=[],
-                idx_blocks=_blocks_to_check(nb, 12, 3), att_heads=[0, 17],
-                att_blocks=_blocks_to_check(nb, 2, 33), seed=3)
+    check_layer(w, est_heads=range(w.heads_q), bs_all_rows_heads=[], bs_rows=[], full_index_heads=[0, 17],
+                idx_blocks=_blocks_to_check(nb, 12, 3), att_heads=[0, 9, 17, 31],
+                att_blocks=_blocks_to_check(nb, 12, 33), dense_heads=[5, 30],
+                dense_blocks=_blocks_to_check(nb, 4, 34))
 
 
+@pytest.mark.timeout(600)
 def test_c4_mixed_256k():
     w = W.C4
     nb = w.n_blocks
@@ -173,15 +279,16 @@ def test_c4_mixed_256k():
     vs_h = [int(h) for h in np.nonzero(pats == W.VSLASH)[0]]
     bs_h = [int(h) for h in np.nonzero(pats == W.BSPARSE)[0]]
     a_h = [int(h) for h in np.nonzero(pats == W.ASHAPE)[0]]
-    check_layer(w, vs_full_heads=vs_h[:2], bs_full_heads=bs_h[:1], bs_rows=_blocks_to_check(nb, 12, 4),
-                idx_blocks=_blocks_to_check(nb, 6, 44), att_heads=[vs_h[0], bs_h[0], a_h[0]],
-                att_blocks=_blocks_to_check(nb, 1, 4), seed=4)
+    check_layer(w, est_heads=vs_h + bs_h[:2], bs_all_rows_heads=bs_h[:1], bs_rows=_blocks_to_check(nb, 12, 4),
+                full_index_heads=[vs_h[0], bs_h[0], a_h[0]], idx_blocks=_blocks_to_check(nb, 6, 44),
+                att_heads=[vs_h[0], vs_h[-1], bs_h[0], a_h[0]], att_blocks=_blocks_to_check(nb, 12, 45))
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_c5_vertical_slash_1m():
     w = W.C5
     nb = w.n_blocks
-    check_layer(w, vs_full_heads=[0, 31], bs_full_heads=[], bs_rows=[],
-                idx_blocks=_blocks_to_check(nb, 4, 5), att_heads=[7],
-                att_blocks=[0, 1, nb // 2, nb - 1], seed=5)
+    check_layer(w, est_heads=[0, 11, 22, 31], bs_all_rows_heads=[], bs_rows=[], full_index_heads=[7],
+                idx_blocks=_blocks_to_check(nb, 4, 5), att_heads=[7, 8, 20, 31],
+                att_blocks=_blocks_to_check(nb, 12, 55), dense_heads=[3],
+                dense_blocks=_blocks_to_check(nb, 2, 56))

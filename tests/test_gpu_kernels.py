@@ -224,11 +224,12 @@ def test_block_estimate(dtype, d, n, top):
                             f"blocks h{h} a{a}")
 
 
-@pytest.mark.parametrize("nb", [700, 1500, 4200])
+@pytest.mark.parametrize("nb", [128, 129, 512, 513, 700, 1024, 1025, 1500, 2048, 2049, 4096, 4097, 4200])
 def test_block_estimate_long_rows(nb):
-    """Rows of 513-1024 and 1025-2048 blocks (16 and 32 register slots per
-    lane in the one-wavefront-per-row select) and above 4096 blocks (the
-    workgroup-per-row select)."""
+    """Every row of layers whose block count sits on each side of the select
+    kernel's dispatch boundaries: one wavefront per row holding 2, 8, 16, 32
+    or 64 register slots per lane (rows of up to 128, 512, 1024, 2048, 4096
+    blocks), and a workgroup per row above 4096 blocks."""
     say(f"block_estimate long rows nb={nb}")
     n, d, top = 64 * nb, 64, 20
     _, (q, k, _), (q64, k64, _) = _inputs(14, 1, 1, n, d, "bf16")
@@ -239,7 +240,7 @@ def test_block_estimate_long_rows(nb):
     tri = np.tril(np.ones((nb, nb), bool))
     assert_scores_close(w[0, 0][tri], rw[tri], "block weights")
     assert not w[0, 0][~tri].any()
-    for a in list(range(0, nb, 37)) + [nb - 1]:
+    for a in range(nb):
         kk = min(top, a + 1)
         assert bcnt[0, 0, a] == kk
         check_selection(bidx[0, 0, a], w[0, 0, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks a{a}")
@@ -324,3 +325,40 @@ def test_schedule_changes_order_not_results(n, hq, hkv, batch):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o3, o4) and torch.equal(l3, l4)
+
+
+@pytest.mark.parametrize("n,hq,hkv,batch,pat", [
+    (64 * 45, 8, 2, 2, [1, 0, 2, 3, 2, 1, 3, 0]),
+    (64 * 13, 4, 4, 1, [0, 1, 2, 3]),
+    (64 * 300, 32, 8, 1, None),
+    (64 * 97, 12, 3, 3, [2, 2, 0, 1, 1, 1, 1, 0, 2, 3, 3, 0]),
+])
+def test_device_schedule_equals_host_schedule(n, hq, hkv, batch, pat):
+    """The schedule the library builds in the workspace on the device is the
+    host's stable sort of the same chunks (mi_attn_schedule), entry for entry."""
+    say(f"device schedule n={n} hq={hq} hkv={hkv} batch={batch}")
+    q = torch.zeros(batch, hq, n, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(batch, hkv, n, 128, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    block_cap = 9
+    idx = None
+    if pat is not None:
+        bcap, ccap = mi.index_caps(n, pat, 30, 40, block_cap, 100, 700)
+        idx = mi.alloc_index(batch, hq, n, bcap, ccap, "cuda")
+        block_cap = bcap
+        # a valid (diagonal-only) index: every row lists its own block
+        nb = n // 64
+        idx.block_count.fill_(1)
+        idx.block_idx.fill_(-1)
+        idx.block_idx[..., 0] = torch.arange(nb, dtype=torch.int32, device="cuda")
+    host = mi.attn_schedule(q, k, pat, 100, 700, block_cap)
+    desc = mi.make_desc(q, k, v, q)
+    ws = torch.full((mi.workspace_bytes(desc, mi.OP_SPARSE_PREFILL),), 0x7f, dtype=torch.uint8, device="cuda")
+    mi.sparse_prefill(q, k, v, pat, idx, sink=100, local=700, workspace=ws)
+    torch.cuda.synchronize()
+    dev = ws[: 4 * len(host)].view(torch.int32).cpu().tolist()
+    assert dev == host
+    nruns = (n // 64 + 3) // 4
+    items = sorted(x for x in host if x >= 0)
+    assert items == list(range(batch * hq * nruns))
+

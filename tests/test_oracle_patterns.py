@@ -201,6 +201,57 @@ def test_bs_block_size_one_is_per_token_topk():
         assert (w[a, a + 1:] == 0).all()
 
 
+def test_bs_weights_block_size_one_equal_library_softmax():
+    """Block size 1: the weights of row a are the library softmax of the
+    scaled per-token logits over keys 0..a (a dropped or doubled scale fails)."""
+    from scipy.special import softmax
+    n, d, scale = 30, 8, 0.37
+    q, k, _ = _rand(21, n, d)
+    w, _ = O.bs_estimate(q, k, scale, 4, block=1)
+    for a in range(n):
+        ref = softmax(np.array([scale * float(np.dot(q[a], k[c])) for c in range(a + 1)]))
+        np.testing.assert_allclose(w[a, : a + 1], ref, rtol=1e-12, atol=1e-15)
+        assert (w[a, a + 1:] == 0).all()
+
+
+def test_bs_weights_pure_python_loops():
+    """Block size 64: pooled means, scaled dot products and the causal block
+    softmax written out as plain Python loops with math.exp."""
+    import math
+    nb, d, scale = 5, 3, 0.61
+    q, k, _ = _rand(22, 64 * nb, d)
+    w, _ = O.bs_estimate(q, k, scale, 2)
+    mean = lambda x, blk, e: sum(float(x[64 * blk + r, e]) for r in range(64)) / 64.0
+    for a in range(nb):
+        qb = [mean(q, a, e) for e in range(d)]
+        z = [scale * sum(qb[e] * mean(k, c, e) for e in range(d)) for c in range(a + 1)]
+        top = max(z)
+        ex = [math.exp(x - top) for x in z]
+        tot = sum(ex)
+        for c in range(nb):
+            ref = ex[c] / tot if c <= a else 0.0
+            assert abs(w[a, c] - ref) <= 1e-13, (a, c, w[a, c], ref)
+
+
+def test_bs_weights_closed_form_on_constant_blocks():
+    """Constant rows per block: Qbar_a = u_a, Kbar_c = t_c exactly, so row a's
+    weights are exp(s u_a.t_c) / sum_c' exp(s u_a.t_c').  With u_a = (1, 0)
+    and t_c = (c, 0): w[a, c] = e^{s c} (e^s - 1) / (e^{s (a+1)} - 1)."""
+    import math
+    nb, s = 6, 0.25
+    q = np.zeros((64 * nb, 2))
+    q[:, 0] = 1.0
+    k = np.zeros((64 * nb, 2))
+    k[:, 0] = np.repeat(np.arange(nb, dtype=float), 64)
+    w, kept = O.bs_estimate(q, k, s, 3)
+    for a in range(nb):
+        for c in range(a + 1):
+            ref = math.exp(s * c) * (math.exp(s) - 1.0) / (math.exp(s * (a + 1)) - 1.0)
+            assert abs(w[a, c] - ref) <= 1e-14, (a, c)
+        # the largest weights are the latest blocks: {0, a} plus a-1
+        assert list(kept[a]) == sorted({0, a} | ({a - 1} if a >= 2 else set()))
+
+
 def test_bs_means_of_constant_blocks():
     d = 4
     k = np.repeat(np.arange(3 * d, dtype=float).reshape(3, d), 64, axis=0)
