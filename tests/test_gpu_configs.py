@@ -172,8 +172,12 @@ def check_layer(w, *, est_heads, bs_all_rows_heads, bs_rows, full_index_heads, i
             a = int(blocks_here[r])
             got_b = bi_h[r, : bc[h, a]]
             got_c = ci_h[r, : cc[h, a]]
-            if not (np.all(bi_h[r, bc[h, a]:] == -1) and np.all(ci_h[r, cc[h, a]:] == -1)):
-                return f"padding h{h} a{a}"
+            # padding: block rows of every indexed head, column rows of
+            # Vertical-Slash heads (the only ones the build writes)
+            if ih.pattern != O.DENSE and not np.all(bi_h[r, bc[h, a]:] == -1):
+                return f"block padding h{h} a{a}"
+            if ih.pattern == O.VSLASH and not np.all(ci_h[r, cc[h, a]:] == -1):
+                return f"column padding h{h} a{a}"
             if ih.pattern == O.ASHAPE and full and a not in idx_blocks:
                 ref_b = _ashape_blocks_closed_form(a, w.sink, w.local)
             else:
