@@ -38,7 +38,7 @@ from __future__ import annotations
 
 import numpy as np
 
-ASHAPE, VSLASH, BSPARSE, DENSE = 0, 1, 2, 3
+ASHAPE, VSLASH, BSPARSE, DENSE, VSLASH_EXACT = 0, 1, 2, 3, 4
 
 
 # ----------------------------------------------------------------------------
@@ -211,6 +211,26 @@ def vs_exact_allowed(i, V, S):
     return np.union1d(V[V <= i], i - S[S <= i])
 
 
+def vs_exact_attention(q, k, v, scale, rows, V, S):
+    """Attention of query rows over their exact Vertical-Slash key sets
+    ([GUIDE] "The Vertical-Slash Pattern"): row i attends to
+    A(i) = {j in V : j <= i} u {i - o : o in S, o <= i}, each key once.
+
+    This is the per-element pattern itself, not its tile covering: the
+    element-masked variant of the sparse kernel is compared with it.
+    Returns (o [R, d], lse [R])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    V = np.unique(np.asarray(V, dtype=np.int64))
+    S = np.unique(np.asarray(S, dtype=np.int64))
+    hi = int(rows.max())
+    diag = (rows[:, None] - S[None, :]).reshape(-1)
+    cand = np.union1d(V[V <= hi], diag[diag >= 0])
+    i = rows[:, None]
+    causal = cand[None, :] <= i
+    mask = causal & (np.isin(cand, V)[None, :] | np.isin(i - cand[None, :], S))
+    return masked_rows_attention(q, k, v, scale, rows, cand, mask)
+
+
 # ----------------------------------------------------------------------------
 # Block-Sparse: mean pooling per 64-token block ([SUM]; [GUIDE] 2.)
 # ----------------------------------------------------------------------------
@@ -298,7 +318,7 @@ class HeadIndex:
         self.V, self.S, self.kept, self.sink, self.local = V, S, kept, sink, local
 
     def blocks(self, a):
-        if self.pattern == VSLASH:
+        if self.pattern in (VSLASH, VSLASH_EXACT):
             return vs_block_list(a, self.S, self.block)
         if self.pattern == BSPARSE:
             return self.kept[a]
@@ -307,7 +327,7 @@ class HeadIndex:
         return np.arange(a + 1)
 
     def cols(self, a):
-        if self.pattern == VSLASH:
+        if self.pattern in (VSLASH, VSLASH_EXACT):
             return vs_column_list(a, self.V, self.blocks(a), self.block)
         return np.zeros(0, np.int64)
 
@@ -323,6 +343,8 @@ def head_attention(q, k, v, scale, idx: HeadIndex, blocks_a):
             out[a] = ashape_attention(q, k, v, scale, rows, idx.sink, idx.local)
         elif idx.pattern == DENSE:
             out[a] = union_attention(q, k, v, scale, rows, np.arange(rows[-1] + 1))
+        elif idx.pattern == VSLASH_EXACT:
+            out[a] = vs_exact_attention(q, k, v, scale, rows, idx.V, idx.S)
         else:
             out[a] = attention_from_index(q, k, v, scale, a, idx.blocks(a), idx.cols(a), bsz)
     return out
@@ -334,10 +356,10 @@ def build_head_index(pattern, q, k, scale, *, last_q=64, n_vertical=1000, n_slas
     """Online index of one head from its own fp64 estimates.
     Returns (HeadIndex, scores dict)."""
     n = k.shape[0]
-    if pattern == VSLASH:
+    if pattern in (VSLASH, VSLASH_EXACT):
         vert, sl = vs_estimate(q, k, scale, last_q)
         V, S = vs_select(vert, sl, n_vertical, n_slash, force_vertical, force_slash)
-        return HeadIndex(VSLASH, n, block, V=V, S=S), dict(vertical=vert, slash=sl)
+        return HeadIndex(pattern, n, block, V=V, S=S), dict(vertical=vert, slash=sl)
     if pattern == BSPARSE:
         w, kept = bs_estimate(q, k, scale, top_blocks, block)
         return HeadIndex(BSPARSE, n, block, kept=kept), dict(w=w)

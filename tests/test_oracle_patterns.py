@@ -187,6 +187,72 @@ def test_vs_index_invariants(seed):
             assert i in u
 
 
+# ---------------------------------------------------------- exact Vertical-Slash set
+
+def test_vs_exact_golden():
+    gold = _read_golden("vs_exact_n10_v04_s03.txt")
+    assert sorted(gold) == list(range(10))
+    for i, keys in gold.items():
+        assert list(O.vs_exact_allowed(i, [0, 4], [0, 3])) == keys
+
+
+def test_vs_exact_attention_matches_golden_rows_and_row_gather():
+    """Block attention over the exact sets equals per-row gathers over the
+    hand-worked key sets."""
+    gold = _read_golden("vs_exact_n10_v04_s03.txt")
+    q, k, v = _rand(31, 10, 6)
+    o, lse = O.vs_exact_attention(q, k, v, 0.4, np.arange(10), [0, 4], [0, 3])
+    for i, keys in gold.items():
+        oi, li = O.attention_row_gather(q, k, v, 0.4, i, keys)
+        np.testing.assert_allclose(o[i], oi, atol=1e-13, rtol=0)
+        assert abs(lse[i] - li) < 1e-13
+
+
+def test_vs_exact_attention_brute_force_mask():
+    """Masked dense softmax with the mask written out by a double loop over
+    (i, j) from the definition: j <= i and (j in V or i - j in S)."""
+    n, d = 96, 8
+    q, k, v = _rand(32, n, d)
+    g = np.random.default_rng(33)
+    V = np.unique(np.concatenate([[0], g.choice(n, 9, replace=False)]))
+    S = np.unique(np.concatenate([[0], g.choice(n, 13, replace=False)]))
+    Vs, Ss = set(int(x) for x in V), set(int(x) for x in S)
+    mask = np.zeros((n, n), bool)
+    for i in range(n):
+        for j in range(i + 1):
+            mask[i, j] = (j in Vs) or ((i - j) in Ss)
+    s = 0.35 * (q @ k.T)
+    s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ref = (p @ v) / p.sum(axis=1, keepdims=True)
+    rows = np.arange(n)
+    o, _ = O.vs_exact_attention(q, k, v, 0.35, rows, V, S)
+    np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
+    # row sizes: |V <= i| + |S <= i| - |{o in S, o <= i : i - o in V}|
+    for i in range(n):
+        both = sum(1 for x in Ss if x <= i and (i - x) in Vs)
+        size = sum(1 for x in Vs if x <= i) + sum(1 for x in Ss if x <= i) - both
+        assert size == mask[i].sum() == len(O.vs_exact_allowed(i, V, S))
+
+
+def test_vs_exact_full_sets_are_dense_and_tiles_contain_it():
+    n, d = 64 * 3, 8
+    q, k, v = _rand(34, n, d)
+    dense, _ = O.dense_causal_attention(q, k, v, 0.3)
+    full = np.arange(n)
+    o, _ = O.vs_exact_attention(q, k, v, 0.3, np.arange(n), full, full)
+    np.testing.assert_allclose(o, dense, atol=1e-12, rtol=0)
+    # exact sets lie inside the tile covering (blocks + columns) of the same V, S
+    g = np.random.default_rng(35)
+    V = np.unique(np.concatenate([[0], g.choice(n, 7, replace=False)]))
+    S = np.unique(np.concatenate([[0], g.choice(n, 11, replace=False)]))
+    idx = O.HeadIndex(O.VSLASH_EXACT, n, V=V, S=S)
+    for a in range(3):
+        u = O.block_union(idx.blocks(a), idx.cols(a))
+        for i in range(64 * a, 64 * a + 64):
+            assert np.isin(O.vs_exact_allowed(i, V, S), u).all()
+
+
 # ---------------------------------------------------------- Block-Sparse
 
 def test_bs_block_size_one_is_per_token_topk():
