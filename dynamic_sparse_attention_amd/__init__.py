@@ -30,7 +30,9 @@ STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_BUDGET", 4
           5: "MI_ERR_WORKSPACE", 6: "MI_ERR_LAUNCH", 7: "MI_ERR_PATTERN"}
 
 EXPORTS = ("mi_workspace_bytes", "mi_vs_estimate", "mi_block_estimate", "mi_build_index",
-           "mi_sparse_prefill", "mi_attn_schedule", "mi_status_str", "mi_last_error")
+           "mi_sparse_prefill", "mi_sparse_prefill_noalloc", "mi_attn_schedule", "mi_status_str",
+           "mi_last_error")
+NOALLOC_SCHEDULE_ENTRIES = 1 << 18
 
 
 class MiError(RuntimeError):
@@ -67,6 +69,8 @@ _SIGS = {
                             ctypes.POINTER(MiIndex), _P]),
     "mi_sparse_prefill": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _P, ctypes.POINTER(MiIndex),
                                _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mi_sparse_prefill_noalloc": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _P, ctypes.POINTER(MiIndex),
+                                       _I, _I, _P, _P, _P]),
     "mi_attn_schedule": (_I, [ctypes.POINTER(MiAttnDesc), _P, _I, _I, _I, _P, _I]),
     "mi_status_str": (ctypes.c_char_p, [_I]),
     "mi_last_error": (ctypes.c_char_p, []),
@@ -290,6 +294,26 @@ def sparse_prefill(q, k, v, head_pattern: Optional[Sequence[int]], index: Option
                                    None if st is None else ctypes.byref(st), sink, local,
                                    _ptr(out), _ptr(lse), None if ws is None else _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def sparse_prefill_noalloc(q, k, v, head_pattern: Optional[Sequence[int]], index: Optional[Index],
+                           sink: int = 128, local: int = 4096, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           stream=None):
+    """sparse_prefill with the item schedule in the library's built-in buffer
+    (mi_sparse_prefill_noalloc): the caller passes preallocated out (and lse
+    or None); nothing is allocated by the call.  Returns (out, lse)."""
+    if out is None:
+        raise ValueError("sparse_prefill_noalloc needs a preallocated out tensor")
+    Hq = q.shape[1]
+    desc = make_desc(q, k, v, out, scale=scale)
+    pat = None if head_pattern is None else (ctypes.c_int32 * Hq)(*[int(p) for p in head_pattern])
+    st = index.c_struct() if index is not None else None
+    _check(lib().mi_sparse_prefill_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           None if pat is None else ctypes.cast(pat, _P),
+                                           None if st is None else ctypes.byref(st), sink, local,
+                                           _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

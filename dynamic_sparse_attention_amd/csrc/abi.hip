@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "mi_internal.h"
@@ -12,6 +13,14 @@
 namespace mi {
 size_t build_index_lds_bytes(int32_t N, int32_t n_slash);
 }
+
+// The built-in schedule buffer of mi_sparse_prefill_noalloc: one copy per
+// GPU, in the library's device globals, held until the process ends.  Host
+// code never passes the array's name to a kernel (in host code it is a
+// host-side stand-in); it uses the device address hipGetSymbolAddress
+// returns, looked up once per device with that device current
+// (scratch_pointer below).
+static __device__ __align__(256) int32_t scratch[MI_NOALLOC_SCHEDULE_ENTRIES];
 
 namespace {
 
@@ -88,6 +97,88 @@ void copy_strides(int64_t* dst, const int64_t* src) {
 
 mi_status launched(hipError_t e) {
     if (e != hipSuccess) return fail(MI_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return MI_OK;
+}
+
+// Validation and argument packing shared by the two attention entry points.
+mi_status prepare_attn(const mi_attn_desc* d, const void* q, const void* k, const void* v,
+                       const int32_t* head_pattern, const mi_index* idx, int32_t sink_tokens,
+                       int32_t local_tokens, void* o, float* lse, mi::AttnArgs& a) {
+    mi_status st = check_desc(d);
+    if (st != MI_OK) return st;
+    if (!q || !k || !v || !o) return fail(MI_ERR_NULL, "q, k, v or o is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(MI_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
+    bool any_sparse = false, any_vs = false, any_a = false;
+    if (head_pattern) {
+        if ((st = check_patterns(d, head_pattern)) != MI_OK) return st;
+        for (int h = 0; h < d->heads_q; ++h) {
+            any_sparse |= head_pattern[h] != MI_DENSE;
+            any_vs |= head_pattern[h] == MI_VSLASH;
+            any_a |= head_pattern[h] == MI_ASHAPE;
+        }
+    }
+    if (any_sparse) {
+        if (!idx || !idx->block_count || !idx->block_idx)
+            return fail(MI_ERR_NULL, "sparse heads need idx with block_count and block_idx");
+        if (idx->block_cap < 1) return fail(MI_ERR_BUDGET, "idx->block_cap must be >= 1");
+        if (any_vs && (!idx->col_count || !idx->col_idx || idx->col_cap < 1))
+            return fail(MI_ERR_NULL, "Vertical-Slash heads need idx->col_count, col_idx and col_cap >= 1");
+    }
+    if (any_a && (sink_tokens < 0 || local_tokens < 1))
+        return fail(MI_ERR_BUDGET, "A-shape needs sink_tokens >= 0 and local_tokens >= 1");
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    copy_strides(a.qs, d->q_stride);
+    copy_strides(a.ks, d->k_stride);
+    copy_strides(a.vs, d->v_stride);
+    copy_strides(a.os, d->o_stride);
+    a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.N = d->seq_len; a.D = d->head_dim;
+    a.dtype = d->dtype; a.scale = d->scale;
+    if (any_sparse) {
+        a.block_count = idx->block_count; a.block_idx = idx->block_idx;
+        a.col_count = idx->col_count; a.col_idx = idx->col_idx;
+        a.block_cap = idx->block_cap; a.col_cap = idx->col_cap;
+    }
+    a.sink = sink_tokens; a.local = local_tokens;
+    a.all_dense = head_pattern ? 0 : 1;
+    for (int h = 0; h < d->heads_q; ++h) a.pattern[h] = head_pattern ? (uint8_t)head_pattern[h] : (uint8_t)MI_DENSE;
+    const size_t es = d->dtype == MI_BF16 ? 2 : 4;
+    if ((uint64_t)d->k_stride[2] * es * MI_BLOCK >= (1ull << 31) || (uint64_t)d->v_stride[2] * es * MI_BLOCK >= (1ull << 31))
+        return fail(MI_ERR_SHAPE, "K/V token strides too large (64 rows must span < 2 GiB)");
+    const size_t lds = mi::sparse_attn_lds_bytes(a);
+    if (lds > mi::kAttnMaxLds)
+        return fail(MI_ERR_SHAPE, "attention needs %zu bytes of LDS (> %zu): seq_len or col_cap too large", lds,
+                    mi::kAttnMaxLds);
+    return MI_OK;
+}
+
+// Builds the item schedule into `sched` (device memory) and launches the
+// attention that reads it, both on stream s.
+mi_status launch_scheduled(mi::AttnArgs& a, int32_t* sched, hipStream_t s) {
+    mi_status st = launched(mi::launch_attn_schedule(a, sched, s));
+    if (st != MI_OK) return st;
+    a.sched = sched;
+    a.sched_len = mi::attn_schedule_len(a);
+    return launched(mi::launch_sparse_attn(a, s));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+mi_status scratch_pointer(int32_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(MI_ERR_LAUNCH, "no current HIP device (or device id >= %d)", kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MI_ERR_LAUNCH, "hipGetSymbolAddress of the schedule buffer failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
     return MI_OK;
 }
 
@@ -256,52 +347,9 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
                             const int32_t* head_pattern, const mi_index* idx, int32_t sink_tokens,
                             int32_t local_tokens, void* o, float* lse, void* ws, size_t ws_bytes,
                             void* stream) {
-    mi_status st = check_desc(d);
-    if (st != MI_OK) return st;
-    if (!q || !k || !v || !o) return fail(MI_ERR_NULL, "q, k, v or o is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-        return fail(MI_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
-    bool any_sparse = false, any_vs = false, any_a = false;
-    if (head_pattern) {
-        if ((st = check_patterns(d, head_pattern)) != MI_OK) return st;
-        for (int h = 0; h < d->heads_q; ++h) {
-            any_sparse |= head_pattern[h] != MI_DENSE;
-            any_vs |= head_pattern[h] == MI_VSLASH;
-            any_a |= head_pattern[h] == MI_ASHAPE;
-        }
-    }
-    if (any_sparse) {
-        if (!idx || !idx->block_count || !idx->block_idx)
-            return fail(MI_ERR_NULL, "sparse heads need idx with block_count and block_idx");
-        if (idx->block_cap < 1) return fail(MI_ERR_BUDGET, "idx->block_cap must be >= 1");
-        if (any_vs && (!idx->col_count || !idx->col_idx || idx->col_cap < 1))
-            return fail(MI_ERR_NULL, "Vertical-Slash heads need idx->col_count, col_idx and col_cap >= 1");
-    }
-    if (any_a && (sink_tokens < 0 || local_tokens < 1))
-        return fail(MI_ERR_BUDGET, "A-shape needs sink_tokens >= 0 and local_tokens >= 1");
     mi::AttnArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    copy_strides(a.qs, d->q_stride);
-    copy_strides(a.ks, d->k_stride);
-    copy_strides(a.vs, d->v_stride);
-    copy_strides(a.os, d->o_stride);
-    a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.N = d->seq_len; a.D = d->head_dim;
-    a.dtype = d->dtype; a.scale = d->scale;
-    if (any_sparse) {
-        a.block_count = idx->block_count; a.block_idx = idx->block_idx;
-        a.col_count = idx->col_count; a.col_idx = idx->col_idx;
-        a.block_cap = idx->block_cap; a.col_cap = idx->col_cap;
-    }
-    a.sink = sink_tokens; a.local = local_tokens;
-    a.all_dense = head_pattern ? 0 : 1;
-    for (int h = 0; h < d->heads_q; ++h) a.pattern[h] = head_pattern ? (uint8_t)head_pattern[h] : (uint8_t)MI_DENSE;
-    const size_t es = d->dtype == MI_BF16 ? 2 : 4;
-    if ((uint64_t)d->k_stride[2] * es * MI_BLOCK >= (1ull << 31) || (uint64_t)d->v_stride[2] * es * MI_BLOCK >= (1ull << 31))
-        return fail(MI_ERR_SHAPE, "K/V token strides too large (64 rows must span < 2 GiB)");
-    const size_t lds = mi::sparse_attn_lds_bytes(a);
-    if (lds > mi::kAttnMaxLds)
-        return fail(MI_ERR_SHAPE, "attention needs %zu bytes of LDS (> %zu): seq_len or col_cap too large", lds,
-                    mi::kAttnMaxLds);
+    mi_status st = prepare_attn(d, q, k, v, head_pattern, idx, sink_tokens, local_tokens, o, lse, a);
+    if (st != MI_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (ws) {
         // the item schedule: built into ws by a kernel on the stream, read by
@@ -309,12 +357,26 @@ mi_status mi_sparse_prefill(const mi_attn_desc* d, const void* q, const void* k,
         const size_t bytes = (size_t)mi::attn_schedule_len(a) * sizeof(int32_t);
         if (ws_bytes < bytes) return fail(MI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, bytes);
         if (!aligned16(ws)) return fail(MI_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-        mi_status st2 = launched(mi::launch_attn_schedule(a, static_cast<int32_t*>(ws), s));
-        if (st2 != MI_OK) return st2;
-        a.sched = static_cast<const int32_t*>(ws);
-        a.sched_len = mi::attn_schedule_len(a);
+        return launch_scheduled(a, static_cast<int32_t*>(ws), s);
     }
     return launched(mi::launch_sparse_attn(a, s));
+}
+
+mi_status mi_sparse_prefill_noalloc(const mi_attn_desc* d, const void* q, const void* k, const void* v,
+                                    const int32_t* head_pattern, const mi_index* idx, int32_t sink_tokens,
+                                    int32_t local_tokens, void* o, float* lse, void* stream) {
+    mi::AttnArgs a{};
+    mi_status st = prepare_attn(d, q, k, v, head_pattern, idx, sink_tokens, local_tokens, o, lse, a);
+    if (st != MI_OK) return st;
+    const int32_t len = mi::attn_schedule_len(a);
+    if (len > MI_NOALLOC_SCHEDULE_ENTRIES)
+        return fail(MI_ERR_WORKSPACE,
+                    "the item schedule needs %d entries, more than the %d of the built-in buffer "
+                    "(batch * heads_q * ceil(seq_len / 256) too large): use mi_sparse_prefill with a workspace",
+                    len, MI_NOALLOC_SCHEDULE_ENTRIES);
+    int32_t* buf = nullptr;
+    if ((st = scratch_pointer(&buf)) != MI_OK) return st;
+    return launch_scheduled(a, buf, static_cast<hipStream_t>(stream));
 }
 
 int32_t mi_attn_schedule(const mi_attn_desc* d, const int32_t* head_pattern, int32_t sink_tokens,

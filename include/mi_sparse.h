@@ -213,6 +213,24 @@ mi_status mi_sparse_prefill(const mi_attn_desc* desc, const void* q, const void*
                             int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* mi_sparse_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the same computation, arguments and errors as mi_sparse_prefill with a
+ * workspace, except that the item schedule is built in a buffer inside the
+ * library instead of a caller workspace.  The buffer holds
+ * MI_NOALLOC_SCHEDULE_ENTRIES int32 entries (1 MiB) per GPU, in the
+ * library's device globals, kept until the process ends; a call whose
+ * schedule needs more entries (about batch * heads_q * seq_len / 256) returns
+ * MI_ERR_WORKSPACE and enqueues nothing.  The call allocates nothing.  Every
+ * call on one GPU writes the same buffer (each call writes every entry it
+ * reads, so nothing needs clearing): calls that overlap on one GPU, on
+ * different streams, race. */
+#define MI_NOALLOC_SCHEDULE_ENTRIES (1 << 18)
+mi_status mi_sparse_prefill_noalloc(const mi_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const int32_t* head_pattern, const mi_index* idx,
+                                    int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
+                                    void* stream);
+
 /* The attention item schedule that mi_sparse_prefill builds in its ws on
  * the device, computed here on the host (host call, no device work, no
  * state kept between calls).  Items are runs of four 64-row query blocks
