@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal comparator")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token secondary measurement")
+    ap.add_argument("--no-exact", action="store_true",
+                    help="skip the exact (element-masked) Vertical-Slash variant and the clustered-slash layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
@@ -98,7 +100,7 @@ def index_work(plan, d):
             tiles += B * nb * (nb + 1) // 2
         else:
             tiles += int(bc[:, h].sum())
-            if p == W.VSLASH:
+            if p in (W.VSLASH, W.VSLASH_EXACT):
                 cols += int(cc[:, h].sum())
     flop = 4.0 * d * 64 * 64 * tiles + 4.0 * d * 64 * cols
     dense_flop = 4.0 * d * B * Hq * (N * (N + 1) / 2)
@@ -126,7 +128,7 @@ def exact_pairs(plan, w):
                         np.maximum(0, i + 1 - np.maximum(i - w.local + 1, w.sink))))
     for b in range(B):
         for h, p in enumerate(plan.pat):
-            if p == W.VSLASH:
+            if p in (W.VSLASH, W.VSLASH_EXACT):
                 V = np.sort(vidx[b, h][vidx[b, h] >= 0]).astype(np.int64)
                 S = np.sort(sidx[b, h][sidx[b, h] >= 0]).astype(np.int64)
                 both = int(np.searchsorted(S, N - 1 - V, side="right").sum())
@@ -198,17 +200,20 @@ def cpu_baseline(w, data, plan, budget_s):
                        f"{elapsed:.1f} s of CPU time")}
 
 
-def measure(w, steps, warmup, dense, keep=False):
+def measure(w, steps, warmup, dense, keep=False, exact=False, data=None):
     """Generates the workload, runs `warmup` untimed and `steps` timed passes
     of the hot path (events around each call, on the stream the library
-    launches on), and optionally times the dense comparator once."""
+    launches on), and optionally times the dense comparator (median of three
+    launches).  exact=True runs the Vertical-Slash heads as exact
+    (element-masked) heads."""
     import torch
     import dynamic_sparse_attention_amd as mi
     import workloads as W
-    log(f"[bench] generating {w.name} (N={w.seq_len}, Hq={w.heads_q}, Hkv={w.heads_kv})")
-    t0 = time.time()
-    data = W.generate(w)
-    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    if data is None:
+        log(f"[bench] generating {w.name} (N={w.seq_len}, Hq={w.heads_q}, Hkv={w.heads_kv})")
+        t0 = time.time()
+        data = W.generate(w)
+        log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     dev = torch.device("cuda:0")
 
     def up(x):
@@ -218,6 +223,8 @@ def measure(w, steps, warmup, dense, keep=False):
 
     q, k, v = up(data["q"]), up(data["k"]), up(data["v"])
     pats = [int(p) for p in data["patterns"]]
+    if exact:
+        pats = [W.VSLASH_EXACT if p == W.VSLASH else p for p in pats]
     if not keep:
         data = {"patterns": data["patterns"]}
     plan = mi.LayerPlan(q, k, v, pats, last_q=w.last_q, n_vertical=w.n_vertical, n_slash=w.n_slash,
@@ -256,18 +263,45 @@ def measure(w, steps, warmup, dense, keep=False):
     nb = w.n_blocks
     res["causal_tiles"] = w.batch * w.heads_q * nb * (nb + 1) // 2
     if dense:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         plan.attention(dense=True)
         torch.cuda.synchronize()
-        e0.record(stream)
-        plan.attention(dense=True)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1)
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            plan.attention(dense=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        dms = float(np.median(times))
         res["dense"] = {"ms": round(dms, 3),
                         "tflops": round(4.0 * w.head_dim * 64 * 64 * res["causal_tiles"] / (dms * 1e-3) / 1e12, 2)}
         log(f"[bench] {w.name}: dense causal attention {dms:.3f} ms")
     return res, plan, data
+
+
+def mi_layer_plan(q, k, v, pats, w):
+    import dynamic_sparse_attention_amd as mi
+    return mi.LayerPlan(q, k, v, pats, last_q=w.last_q, n_vertical=w.n_vertical, n_slash=w.n_slash,
+                        force_vertical=w.force_vertical, force_slash=w.force_slash,
+                        top_blocks=w.top_blocks, sink=w.sink, local=w.local)
+
+
+def time_attention(plan, launches):
+    """Median of `launches` timed attention launches of a plan whose index is built."""
+    import torch
+    stream = torch.cuda.current_stream()
+    plan.attention()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan.attention()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
 
 
 def exact_summary(r, d):
@@ -332,7 +366,39 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, data, plan, args.cpu_seconds)
+    if not args.no_exact and any(p == W.VSLASH for p in plan.pat):
+        # the same layer with the Vertical-Slash heads element-masked to their
+        # exact key sets: attention time on the same estimate and index lists
+        q, k, v = plan.q, plan.k, plan.v
+        ex = mi_layer_plan(q, k, v, [W.VSLASH_EXACT if p == W.VSLASH else p for p in plan.pat], w)
+        ex.run()
+        torch.cuda.synchronize()
+        ems = time_attention(ex, 3)
+        out["exact_variant"] = {
+            "attention_ms": round(ems, 3), "aligned_attention_ms": round(r["att_ms"], 3),
+            "effective_tflops": round(4.0 * d * r["exact_pairs"] / (ems * 1e-3) / 1e12, 2),
+            "aligned_effective_tflops": out["exact_pattern"]["effective_tflops"]}
+        log(f"[bench] {w.name}: exact variant attention {ems:.3f} ms")
+        del ex
     del plan, data
+    if not args.no_exact and args.config == "c3":
+        # the clustered-slash variant of the layer: aligned tiles vs exact
+        torch.cuda.empty_cache()
+        wl = W.WORKLOADS["c3local"]
+        rl, pl, dl = measure(wl, 5, 2, False, keep=True)
+        del pl
+        re_, pe, _ = measure(wl, 5, 2, False, exact=True, data=dl)
+        del pe, dl
+        out["clustered_slash"] = {
+            "workload": wl.name, "seq_len": wl.seq_len,
+            "aligned": {"ms_per_layer": round(rl["ms_step"], 3), "attention_ms": round(rl["att_ms"], 3),
+                        "index": {"tiles": rl["tiles"], "columns": rl["cols"],
+                                  "tile_density": round(rl["tiles"] / rl["causal_tiles"], 4)},
+                        "exact_pattern": exact_summary(rl, wl.head_dim)},
+            "exact": {"ms_per_layer": round(re_["ms_step"], 3), "attention_ms": round(re_["att_ms"], 3),
+                      "effective_tflops": round(4.0 * wl.head_dim * re_["exact_pairs"] /
+                                                (re_["att_ms"] * 1e-3) / 1e12, 2)},
+        }
     if not args.no_1m and args.config == "c3":
         torch.cuda.empty_cache()
         w5 = W.WORKLOADS["c5"]

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_PKG, "libmi_sparse.so")
 MI_BLOCK = 64
 MI_MAX_HEADS = 256
 MI_F32, MI_BF16 = 0, 1
-ASHAPE, VSLASH, BSPARSE, DENSE = 0, 1, 2, 3
+ASHAPE, VSLASH, BSPARSE, DENSE, VSLASH_EXACT = 0, 1, 2, 3, 4
+VS_PATTERNS = (VSLASH, VSLASH_EXACT)
 OP_VS_ESTIMATE, OP_BLOCK_ESTIMATE, OP_SPARSE_PREFILL = 0, 1, 2
 STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_BUDGET", 4: "MI_ERR_DTYPE",
           5: "MI_ERR_WORKSPACE", 6: "MI_ERR_LAUNCH", 7: "MI_ERR_PATTERN"}
@@ -52,7 +53,7 @@ class MiAttnDesc(ctypes.Structure):
 class MiIndex(ctypes.Structure):
     _fields_ = [("block_count", ctypes.c_void_p), ("block_idx", ctypes.c_void_p),
                 ("col_count", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-                ("block_cap", ctypes.c_int32), ("col_cap", ctypes.c_int32)]
+                ("block_cap", ctypes.c_int32), ("col_cap", ctypes.c_int32), ("vs_bits", ctypes.c_void_p)]
 
 
 _lib = None
@@ -208,6 +209,7 @@ class Index:
     block_idx: torch.Tensor    # [B, Hq, nb, block_cap]
     col_count: torch.Tensor    # [B, Hq, nb]
     col_idx: torch.Tensor      # [B, Hq, nb, col_cap]
+    vs_bits: Optional[torch.Tensor] = None  # [B, Hq, 2, N/32 + 4] int32 maps of exact VS heads
 
     @property
     def block_cap(self):
@@ -222,6 +224,7 @@ class Index:
         s.block_count, s.block_idx = self.block_count.data_ptr(), self.block_idx.data_ptr()
         s.col_count, s.col_idx = self.col_count.data_ptr(), self.col_idx.data_ptr()
         s.block_cap, s.col_cap = self.block_cap, self.col_cap
+        s.vs_bits = self.vs_bits.data_ptr() if self.vs_bits is not None else None
         return s
 
 
@@ -231,7 +234,7 @@ def index_caps(n: int, patterns, n_vertical: int = 0, n_slash: int = 0, top_bloc
     nb = n // MI_BLOCK
     pats = set(int(p) for p in patterns)
     bcap, ccap = 1, 1
-    if VSLASH in pats:
+    if pats & set(VS_PATTERNS):
         bcap = max(bcap, min(nb, 2 * n_slash))
         ccap = max(ccap, min(n_vertical, n))
     if BSPARSE in pats:
@@ -241,13 +244,16 @@ def index_caps(n: int, patterns, n_vertical: int = 0, n_slash: int = 0, top_bloc
     return bcap, ccap
 
 
-def alloc_index(B: int, Hq: int, n: int, block_cap: int, col_cap: int, device) -> Index:
+def alloc_index(B: int, Hq: int, n: int, block_cap: int, col_cap: int, device, exact: bool = False) -> Index:
+    """Index buffers; exact=True adds the membership maps of exact
+    Vertical-Slash heads."""
     nb = n // MI_BLOCK
     return Index(
         torch.zeros((B, Hq, nb), dtype=torch.int32, device=device),
         torch.zeros((B, Hq, nb, block_cap), dtype=torch.int32, device=device),
         torch.zeros((B, Hq, nb), dtype=torch.int32, device=device),
-        torch.zeros((B, Hq, nb, max(col_cap, 1)), dtype=torch.int32, device=device))
+        torch.zeros((B, Hq, nb, max(col_cap, 1)), dtype=torch.int32, device=device),
+        torch.zeros((B, Hq, 2, n // 32 + 4), dtype=torch.int32, device=device) if exact else None)
 
 
 def build_index(q, k, head_pattern: Sequence[int], vertical_idx=None, slash_idx=None,
@@ -260,7 +266,7 @@ def build_index(q, k, head_pattern: Sequence[int], vertical_idx=None, slash_idx=
     ns = int(slash_idx.shape[-1]) if slash_idx is not None else 0
     if index is None:
         bcap, ccap = index_caps(N, head_pattern, nv, ns, top_blocks, sink, local)
-        index = alloc_index(B, Hq, N, bcap, ccap, q.device)
+        index = alloc_index(B, Hq, N, bcap, ccap, q.device, exact=VSLASH_EXACT in [int(p) for p in head_pattern])
     pat = (ctypes.c_int32 * Hq)(*[int(p) for p in head_pattern])
     st = index.c_struct()
     _check(lib().mi_build_index(ctypes.byref(desc), ctypes.cast(pat, _P), _ptr(vertical_idx), nv,
@@ -339,7 +345,7 @@ def layer_prefill(q, k, v, head_pattern: Sequence[int], *, last_q=64, n_vertical
     """One layer's whole hot path: estimates for the VS and BS heads, the
     index, and the sparse attention, all enqueued on one stream."""
     pat = [int(p) for p in head_pattern]
-    vs_heads = [h for h, p in enumerate(pat) if p == VSLASH]
+    vs_heads = [h for h, p in enumerate(pat) if p in VS_PATTERNS]
     bs_heads = [h for h, p in enumerate(pat) if p == BSPARSE]
     vidx = sidx = bidx = bcnt = None
     if vs_heads:
@@ -370,7 +376,7 @@ class LayerPlan:
                        force_vertical=force_vertical, force_slash=force_slash,
                        top_blocks=top_blocks, sink=sink, local=local)
         self.scale = scale
-        self.vs_heads = [h for h, p in enumerate(self.pat) if p == VSLASH]
+        self.vs_heads = [h for h, p in enumerate(self.pat) if p in VS_PATTERNS]
         self.bs_heads = [h for h, p in enumerate(self.pat) if p == BSPARSE]
         self.desc = make_desc(q, k, scale=scale)
         self.vidx = self.sidx = self.bidx = self.bcnt = None
@@ -386,7 +392,7 @@ class LayerPlan:
             self.bs_ws = _workspace(workspace_bytes(self.desc, OP_BLOCK_ESTIMATE, len(self.bs_heads)), dev)
             self.bs_heads_c = _heads_arr(self.bs_heads)
         bcap, ccap = index_caps(N, self.pat, n_vertical, n_slash, top_blocks, sink, local)
-        self.index = alloc_index(B, Hq, N, bcap, ccap, dev)
+        self.index = alloc_index(B, Hq, N, bcap, ccap, dev, exact=VSLASH_EXACT in self.pat)
         self.index_c = self.index.c_struct()
         self.pat_c = (ctypes.c_int32 * Hq)(*self.pat)
         self.o = torch.empty_like(q)

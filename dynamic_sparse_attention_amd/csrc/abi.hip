@@ -81,7 +81,7 @@ mi_status check_heads(const mi_attn_desc* d, const int32_t* heads, int32_t n_hea
 
 mi_status check_patterns(const mi_attn_desc* d, const int32_t* pat) {
     for (int h = 0; h < d->heads_q; ++h)
-        if (pat[h] < MI_ASHAPE || pat[h] > MI_DENSE)
+        if (pat[h] < MI_ASHAPE || pat[h] > MI_VSLASH_EXACT)
             return fail(MI_ERR_PATTERN, "head_pattern[%d] = %d is not a pattern code", h, pat[h]);
     return MI_OK;
 }
@@ -109,12 +109,13 @@ mi_status prepare_attn(const mi_attn_desc* d, const void* q, const void* k, cons
     if (!q || !k || !v || !o) return fail(MI_ERR_NULL, "q, k, v or o is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(MI_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
-    bool any_sparse = false, any_vs = false, any_a = false;
+    bool any_sparse = false, any_vs = false, any_a = false, any_exact = false;
     if (head_pattern) {
         if ((st = check_patterns(d, head_pattern)) != MI_OK) return st;
         for (int h = 0; h < d->heads_q; ++h) {
             any_sparse |= head_pattern[h] != MI_DENSE;
-            any_vs |= head_pattern[h] == MI_VSLASH;
+            any_vs |= head_pattern[h] == MI_VSLASH || head_pattern[h] == MI_VSLASH_EXACT;
+            any_exact |= head_pattern[h] == MI_VSLASH_EXACT;
             any_a |= head_pattern[h] == MI_ASHAPE;
         }
     }
@@ -124,6 +125,7 @@ mi_status prepare_attn(const mi_attn_desc* d, const void* q, const void* k, cons
         if (idx->block_cap < 1) return fail(MI_ERR_BUDGET, "idx->block_cap must be >= 1");
         if (any_vs && (!idx->col_count || !idx->col_idx || idx->col_cap < 1))
             return fail(MI_ERR_NULL, "Vertical-Slash heads need idx->col_count, col_idx and col_cap >= 1");
+        if (any_exact && !idx->vs_bits) return fail(MI_ERR_NULL, "exact Vertical-Slash heads need idx->vs_bits");
     }
     if (any_a && (sink_tokens < 0 || local_tokens < 1))
         return fail(MI_ERR_BUDGET, "A-shape needs sink_tokens >= 0 and local_tokens >= 1");
@@ -138,6 +140,7 @@ mi_status prepare_attn(const mi_attn_desc* d, const void* q, const void* k, cons
         a.block_count = idx->block_count; a.block_idx = idx->block_idx;
         a.col_count = idx->col_count; a.col_idx = idx->col_idx;
         a.block_cap = idx->block_cap; a.col_cap = idx->col_cap;
+        a.vs_bits = any_exact ? idx->vs_bits : nullptr;
     }
     a.sink = sink_tokens; a.local = local_tokens;
     a.all_dense = head_pattern ? 0 : 1;
@@ -296,9 +299,10 @@ mi_status mi_build_index(const mi_attn_desc* d, const int32_t* head_pattern, con
     if (!out || !out->block_count || !out->block_idx || !out->col_count)
         return fail(MI_ERR_NULL, "out, out->block_count, out->block_idx or out->col_count is NULL");
     const int nb = d->seq_len / MI_BLOCK;
-    bool any_vs = false, any_bs = false, any_a = false;
+    bool any_vs = false, any_bs = false, any_a = false, any_exact = false;
     for (int h = 0; h < d->heads_q; ++h) {
-        any_vs |= head_pattern[h] == MI_VSLASH;
+        any_vs |= head_pattern[h] == MI_VSLASH || head_pattern[h] == MI_VSLASH_EXACT;
+        any_exact |= head_pattern[h] == MI_VSLASH_EXACT;
         any_bs |= head_pattern[h] == MI_BSPARSE;
         any_a |= head_pattern[h] == MI_ASHAPE;
     }
@@ -315,6 +319,7 @@ mi_status mi_build_index(const mi_attn_desc* d, const int32_t* head_pattern, con
             return fail(MI_ERR_BUDGET, "col_cap %d < min(n_vertical, seq_len) = %d", out->col_cap, need_c);
         const size_t lds = mi::build_index_lds_bytes(d->seq_len, n_slash);
         if (lds > kMaxLds) return fail(MI_ERR_SHAPE, "index build needs %zu bytes of LDS", lds);
+        if (any_exact && !out->vs_bits) return fail(MI_ERR_NULL, "exact Vertical-Slash heads need out->vs_bits");
     }
     if (any_bs) {
         if (!bs_block_idx || !bs_block_count)
@@ -340,6 +345,7 @@ mi_status mi_build_index(const mi_attn_desc* d, const int32_t* head_pattern, con
     a.block_count = out->block_count; a.block_idx = out->block_idx;
     a.col_count = out->col_count; a.col_idx = out->col_idx;
     a.block_cap = out->block_cap; a.col_cap = out->col_cap;
+    a.vs_bits = any_exact ? out->vs_bits : nullptr;
     return launched(mi::launch_build_index(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -16,6 +16,9 @@
 //    which is ascending.  Columns: verticals j <= 64a+63 whose key block is
 //    not a listed tile, in the order of the (ascending) vertical list, by an
 //    ordered wave-ballot compaction.
+//    Exact Vertical-Slash heads get the same lists, plus membership maps of
+//    their vertical keys and slash offsets (vs_bits_kernel) from which the
+//    attention masks each element of a listed tile.
 //  Block-Sparse: copy of the estimated lists.
 //  A-shape: sink blocks [0, ceil(sink/64)) and window blocks
 //    [a - floor((local+62)/64), a], merged.
@@ -84,7 +87,7 @@ __global__ void __launch_bounds__(kTS) tile_set_kernel(IdxP P) {
     const int nb = P.nb;
     const int bh = blockIdx.x;
     const int b = bh / A.Hq, h = bh % A.Hq;
-    if (A.pattern[h] != MI_VSLASH) return;
+    if (A.pattern[h] != MI_VSLASH && A.pattern[h] != MI_VSLASH_EXACT) return;
     const int t = threadIdx.x;
     const int fw = flag_words(nb);
     uint8_t* flag = reinterpret_cast<uint8_t*>(dyn);
@@ -272,6 +275,33 @@ __global__ void __launch_bounds__(kNT) build_index_kernel(IdxP P) {
     }
 }
 
+// Membership maps of an exact Vertical-Slash head (one workgroup per head):
+// words [0, W) hold bit 64 + j for each vertical key j, words [W, 2W) bit
+// 64 + o for each slash offset o (W = N/32 + 4; the first 64 bits and the
+// tail stay zero).  Cleared, then set with atomic ORs.
+__global__ void __launch_bounds__(kTS) vs_bits_kernel(IdxP P) {
+    const IndexArgs& A = P.a;
+    const int bh = blockIdx.x;
+    const int b = bh / A.Hq, h = bh % A.Hq;
+    if (A.pattern[h] != MI_VSLASH_EXACT) return;
+    const int W = A.N / 32 + 4;
+    uint32_t* vb = A.vs_bits + (int64_t)bh * 2 * W;
+    uint32_t* sb = vb + W;
+    const int t = threadIdx.x;
+    for (int w = t; w < 2 * W; w += kTS) vb[w] = 0u;
+    __syncthreads();
+    const int32_t* V = A.vertical_idx + ((int64_t)b * A.Hq + h) * A.n_vertical;
+    const int32_t* S = A.slash_idx + ((int64_t)b * A.Hq + h) * A.n_slash;
+    for (int i = t; i < A.n_vertical; i += kTS) {
+        const int j = V[i];
+        if (j >= 0 && j < A.N) atomicOr(vb + ((j + 64) >> 5), 1u << ((j + 64) & 31));
+    }
+    for (int i = t; i < A.n_slash; i += kTS) {
+        const int o = S[i];
+        if (o >= 0 && o < A.N) atomicOr(sb + ((o + 64) >> 5), 1u << ((o + 64) & 31));
+    }
+}
+
 }  // namespace
 
 size_t build_index_lds_bytes(int32_t N, int32_t n_slash) {
@@ -285,7 +315,11 @@ hipError_t launch_build_index(const IndexArgs& a, hipStream_t s) {
     p.a = a;
     p.nb = a.N / 64;
     bool any_vs = false;
-    for (int h = 0; h < a.Hq; ++h) any_vs |= a.pattern[h] == MI_VSLASH;
+    bool any_exact = false;
+    for (int h = 0; h < a.Hq; ++h) {
+        any_vs |= a.pattern[h] == MI_VSLASH || a.pattern[h] == MI_VSLASH_EXACT;
+        any_exact |= a.pattern[h] == MI_VSLASH_EXACT;
+    }
     p.t_cap = any_vs ? min(p.nb, 2 * a.n_slash) : 0;
     const size_t dyn = any_vs ? build_index_lds_bytes(a.N, a.n_slash) : 0;
     if (dyn > 48 * 1024) {
@@ -303,6 +337,7 @@ hipError_t launch_build_index(const IndexArgs& a, hipStream_t s) {
     }
     const int runs = (p.nb + kAPerWG - 1) / kAPerWG;
     hipLaunchKernelGGL(build_index_kernel, dim3(a.B * a.Hq * runs), dim3(kNT), dyn, s, p);
+    if (any_exact) hipLaunchKernelGGL(vs_bits_kernel, dim3(a.B * a.Hq), dim3(kTS), 0, s, p);
     return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ struct AttnArgs {
     uint8_t pattern[MI_MAX_HEADS];
     const int32_t* sched;  // device item schedule (NULL: the default order)
     int32_t sched_len;     // entries (a multiple of 4)
+    const uint32_t* vs_bits;  // membership maps of exact Vertical-Slash heads (mi_index.vs_bits)
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 // Item schedule of the attention kernel (schedule.hip): bytes (an upper
@@ -120,6 +121,7 @@ struct IndexArgs {
     int32_t* col_count;
     int32_t* col_idx;
     int32_t block_cap, col_cap;
+    uint32_t* vs_bits;
 };
 hipError_t launch_build_index(const IndexArgs& a, hipStream_t s);
 

@@ -49,7 +49,7 @@
 namespace mi {
 namespace {
 
-enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskAShape = 2, kMaskColumns = 3 };
+enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskAShape = 2, kMaskColumns = 3, kMaskExact = 4 };
 
 struct Params {
     const char* q;
@@ -71,6 +71,8 @@ struct Params {
     int32_t xcd_chunk;
     const int32_t* sched;  // item schedule: packed (b * Hq + h) * nruns + run, -1 = none
     int32_t sched_len;
+    const uint32_t* vs_bits;  // exact Vertical-Slash heads: [B, Hq, 2, bits_words] membership maps
+    int32_t bits_words;
     uint8_t pattern[MI_MAX_HEADS];
 };
 
@@ -253,7 +255,7 @@ __device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, 
             }
     }
     int nsteps = ntiles;
-    if (pattern == MI_VSLASH) {
+    if (pattern == MI_VSLASH || pattern == MI_VSLASH_EXACT) {
         int32_t* colsl = reinterpret_cast<int32_t*>(dyn);
         for (int w = 0; w < kBlocks; ++w) {
             const int cnt = w < nblk ? min(max(ld_uniform(p.col_count + r0 + w), 0), p.col_cap) : 0;
@@ -380,8 +382,10 @@ struct RowState {
 };
 
 // Mask mode of a step for the query block `my_a`.
+template <bool EXACT>
 __device__ __forceinline__ int step_mode(uint32_t w, const Params& p, int pattern, int my_a) {
     if (step_col(w)) return kMaskColumns;
+    if (EXACT && pattern == MI_VSLASH_EXACT) return kMaskExact;
     const int kb = step_kb(w);
     if (pattern == MI_ASHAPE) {
         const bool full = kb < my_a && ((kb * 64 + 63 < p.sink) || ((my_a - kb) * 64 + 63 < p.local));
@@ -448,11 +452,62 @@ __device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, cons
     }
 }
 
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+__device__ __forceinline__ uint32_t ld_uniform_u32(const uint32_t* p) {
+    return *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Exact Vertical-Slash mask of a tile step (key block kb): row i keeps key
+// j = 64 kb + c iff j <= i and (j is a vertical key or i - j a slash offset).
+// The maps hold bit x for key / offset x - 64 (64 leading zero bits, so the
+// offsets of keys above the diagonal, down to -63, read as absent).  The
+// wavefront's 32 rows i0 .. i0+31 need the slash offsets
+// [i0 - 64kb - 63, i0 - 64kb + 31]: four words read on the scalar unit, from
+// which each lane funnel-shifts its 64-bit window (bit t <-> offset
+// i - 64kb - 63 + t <-> key c = 63 - t) and bit-reverses it into key order.
+// The vertical bits of the tile's 64 keys are two uniform words.
+__device__ __forceinline__ void mask_exact(f32x16 (&s)[2], const uint32_t* vbits, const uint32_t* sbits, int kb,
+                                           int i0, int i_row) {
+    const int hl = (threadIdx.x >> 5) & 1;
+    const uint32_t v0 = ld_uniform_u32(vbits + 2 * kb + 2), v1 = ld_uniform_u32(vbits + 2 * kb + 3);
+    const int bit0 = i0 - 64 * kb + 1;  // map bit of offset i0 - 64kb - 63 (>= 1 for kb <= the row's block)
+    const int w0 = bit0 >> 5;
+    const uint32_t x0 = ld_uniform_u32(sbits + w0), x1 = ld_uniform_u32(sbits + w0 + 1);
+    const uint32_t x2 = ld_uniform_u32(sbits + w0 + 2), x3 = ld_uniform_u32(sbits + w0 + 3);
+    const int sh = (bit0 & 31) + (i_row - i0);  // 0 .. 62
+    const bool up = sh >= 32;
+    const uint32_t a0 = up ? x1 : x0, a1 = up ? x2 : x1, a2 = up ? x3 : x2;
+    const uint32_t lo = __builtin_amdgcn_alignbit(a1, a0, sh & 31);
+    const uint32_t hi = __builtin_amdgcn_alignbit(a2, a1, sh & 31);
+    uint32_t k_lo = __builtin_bitreverse32(hi) | v0;  // keys 0..31 of the tile
+    uint32_t k_hi = __builtin_bitreverse32(lo) | v1;  // keys 32..63
+    const int lim = i_row - 64 * kb;                  // causal: keys c <= lim (lim < 63 only on the diagonal)
+    if (lim < 63) {
+        k_lo &= lim >= 31 ? ~0u : ((2u << lim) - 1u);
+        k_hi &= lim >= 32 ? ((2u << (lim - 32)) - 1u) : 0u;
+    }
+    // lane half hl holds keys 4 hl + {0..3} of each group of 8
+    const uint32_t m_lo = hl ? (k_lo >> 4) | (k_hi << 28) : k_lo;
+    const uint32_t m_hi = hl ? (k_hi >> 4) : k_hi;
+    const uint32_t ninf = 0xff800000u;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+        const uint32_t m = kh ? m_hi : m_lo;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int bit = 8 * (e >> 2) + (e & 3);
+            const uint32_t keep = (uint32_t)((int32_t)(m << (31 - bit)) >> 31);  // all ones iff the bit is set
+            s[kh][e] = __uint_as_float((__float_as_uint(s[kh][e]) & keep) | (ninf & ~keep));
+        }
+    }
+}
+
 // Masks one row block's scores (element e of half kh is key 32 kh + 8 (e/4) +
 // 4 hl + e%4 of the step).
 // Column steps read each slot's key position from `cl`.
+template <bool EXACT>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int mode, int kb, const int32_t* cl,
-                                            const Params& p, int i_row) {
+                                            const Params& p, int i_row, const uint32_t* ex_bits, int ex_i0) {
     const int hl = (threadIdx.x >> 5) & 1;
     // Opaque copies: the phase code appears once per group, and without
     // these the compiler merges the two copies' comparisons and hoists them
@@ -482,6 +537,8 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int mode, int kb, co
                 const bool keep = (klc <= lim) && ((klc < sl) || (klc > ll));
                 s[kh][e] = keep ? s[kh][e] : -INFINITY;
             }
+    } else if (EXACT && mode == kMaskExact) {
+        if constexpr (EXACT) mask_exact(s, ex_bits, ex_bits + p.bits_words, kb, ex_i0, i_row);
     } else if (mode == kMaskColumns) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -640,7 +697,10 @@ __device__ __forceinline__ void unpark_p(f32x8 (&pf)[2][2], const f32x16 (&s)[2]
 // Barrier that does not wait for outstanding global->LDS copies.
 __device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); }
 
-template <typename T, int D>
+// EXACT: the instantiation launched when some head is MI_VSLASH_EXACT (its
+// tile steps take the per-element Vertical-Slash mask); the other
+// instantiation carries no code for it.
+template <typename T, int D, bool EXACT>
 __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     typedef typename Elem<T>::frag Frag;
     typedef Layout<T, D> Ly;
@@ -674,6 +734,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int kvh = h / p.group;
     const int pattern = p.all_dense ? MI_DENSE : p.pattern[h];
+    const uint32_t* ex_bits = EXACT ? p.vs_bits + (int64_t)(b * p.Hq + h) * 2 * p.bits_words : nullptr;
 
     const int lane = threadIdx.x & 63;
     // wave-uniform: lets all per-wave control live in SGPRs
@@ -756,7 +817,8 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
                 }
                 if (s_need) {
                     s_compute<T, D>(s, kcur, lbo, qf);
-                    mask_scores(s, step_mode(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row);
+                    mask_scores<EXACT>(s, step_mode<EXACT>(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row,
+                                ex_bits, my_a * 64 + (wave & 1) * 32);
                 }
             } else {
                 // Vector phase: V(t-1) for group 1, V(t) for group 0.  The
@@ -832,15 +894,15 @@ size_t lds_bytes_t(int nb, int cstride) {
     return (size_t)Arena<T, D>::kStatic + (size_t)Arena<T, D>::bytes(nb, cstride);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool EXACT>
 hipError_t launch_t(const Params& p, hipStream_t s) {
     const int items = p.sched ? p.sched_len : p.B * p.Hq * p.nruns;
     const size_t dyn = lds_bytes_t<T, D>(p.nb, p.cstride) - Arena<T, D>::kStatic;
     if (dyn + Arena<T, D>::kStatic > kAttnMaxLds) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D, EXACT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D>), dim3(items), dim3(kThreads), dyn, s, p);
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, EXACT>), dim3(items), dim3(kThreads), dyn, s, p);
     return hipGetLastError();
 }
 
@@ -848,7 +910,8 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
 
 int attn_col_stride(const AttnArgs& a) {
     bool any_vs = false;
-    for (int h = 0; h < a.Hq; ++h) any_vs |= !a.all_dense && a.pattern[h] == MI_VSLASH;
+    for (int h = 0; h < a.Hq; ++h)
+        any_vs |= !a.all_dense && (a.pattern[h] == MI_VSLASH || a.pattern[h] == MI_VSLASH_EXACT);
     return any_vs ? (a.col_cap + 63) / 64 * 64 : 0;
 }
 
@@ -882,11 +945,17 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     p.xcd_chunk = p.group;
     p.sched = a.sched;
     p.sched_len = a.sched_len;
+    bool any_exact = false;
     for (int i = 0; i < MI_MAX_HEADS; ++i) p.pattern[i] = a.pattern[i];
+    for (int h = 0; h < a.Hq; ++h) any_exact |= !a.all_dense && a.pattern[h] == MI_VSLASH_EXACT;
+    p.vs_bits = a.vs_bits;
+    p.bits_words = a.N / 32 + 4;
     if (a.dtype == MI_BF16) {
-        return a.D == 128 ? launch_t<uint16_t, 128>(p, s) : launch_t<uint16_t, 64>(p, s);
+        if (any_exact) return a.D == 128 ? launch_t<uint16_t, 128, true>(p, s) : launch_t<uint16_t, 64, true>(p, s);
+        return a.D == 128 ? launch_t<uint16_t, 128, false>(p, s) : launch_t<uint16_t, 64, false>(p, s);
     }
-    return a.D == 128 ? launch_t<float, 128>(p, s) : launch_t<float, 64>(p, s);
+    if (any_exact) return a.D == 128 ? launch_t<float, 128, true>(p, s) : launch_t<float, 64, true>(p, s);
+    return a.D == 128 ? launch_t<float, 128, false>(p, s) : launch_t<float, 64, false>(p, s);
 }
 
 }  // namespace mi

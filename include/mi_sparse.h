@@ -60,8 +60,13 @@ typedef enum { MI_F32 = 0, MI_BF16 = 1 } mi_dtype;
 
 /* Per-head pattern codes.  MI_DENSE (plain causal attention) is not one of the
  * method's patterns; it is the comparator the sparse kernel is measured
- * against and a safe choice for heads that fit no pattern. */
-typedef enum { MI_ASHAPE = 0, MI_VSLASH = 1, MI_BSPARSE = 2, MI_DENSE = 3 } mi_pattern;
+ * against and a safe choice for heads that fit no pattern.  MI_VSLASH runs a
+ * Vertical-Slash head on whole aligned 64x64 tiles (the tiles its slash lines
+ * cross) plus gathered vertical columns; MI_VSLASH_EXACT runs it on the same
+ * tiles masked element by element to the pattern's exact key set (aifetchly
+ * guide, "The Vertical-Slash Pattern": vertical keys every later query
+ * attends to, slash lines at fixed offsets i - j). */
+typedef enum { MI_ASHAPE = 0, MI_VSLASH = 1, MI_BSPARSE = 2, MI_DENSE = 3, MI_VSLASH_EXACT = 4 } mi_pattern;
 
 /* Workspace-sized operations for mi_workspace_bytes(). */
 typedef enum { MI_OP_VS_ESTIMATE = 0, MI_OP_BLOCK_ESTIMATE = 1, MI_OP_SPARSE_PREFILL = 2 } mi_op;
@@ -81,9 +86,15 @@ typedef struct {
  *   block_idx   [batch, heads_q, nb, block_cap]  key-block ids, ascending, padded with -1
  *   col_count   [batch, heads_q, nb]             number of gathered key columns
  *   col_idx     [batch, heads_q, nb, col_cap]    key positions, ascending, padded with -1
+ *   vs_bits     [batch, heads_q, 2, MI_VS_BITS_WORDS(seq_len)] uint32, or NULL
+ *               when no head is MI_VSLASH_EXACT: per exact head, a map of its
+ *               vertical keys (bit 64 + j) then a map of its slash offsets
+ *               (bit 64 + o); the first 64 bits of each map are zero
  * Query block a of a head attends, for each row i, to the keys j <= i that lie
- * in a listed key block or are listed columns.  A listed column never lies in
- * a listed key block. */
+ * in a listed key block or are listed columns (MI_VSLASH_EXACT heads: inside
+ * listed key blocks, only keys j that are vertical keys or whose offset i - j
+ * is a slash offset).  A listed column never lies in a listed key block. */
+#define MI_VS_BITS_WORDS(seq_len) ((seq_len) / 32 + 4)
 typedef struct {
     int32_t* block_count;
     int32_t* block_idx;
@@ -91,6 +102,7 @@ typedef struct {
     int32_t* col_idx;
     int32_t block_cap;
     int32_t col_cap;
+    uint32_t* vs_bits;
 } mi_index;
 
 /* Bytes of workspace an operation needs.  op = MI_OP_VS_ESTIMATE: p0 = number
@@ -161,11 +173,14 @@ mi_status mi_block_estimate(const mi_attn_desc* desc, const void* q, const void*
  * coalesced chunks; "2. The Block-Sparse Kernel Mechanics": only active
  * 64x64 tiles run on the matrix units).  Writes `out` for every head, by
  * head_pattern[h] (HOST int32[heads_q]):
- *   MI_VSLASH : slash offsets S (slash_idx row, -1 entries ignored) become the
+ *   MI_VSLASH, MI_VSLASH_EXACT :
+ *               slash offsets S (slash_idx row, -1 entries ignored) become the
  *               tile distances T = {floor(o/64), ceil(o/64) : o in S};
  *               block list of a = {a - t : t in T, t <= a};
  *               column list of a = {j in V : j <= 64a + 63, block of j not
  *               listed}, V = vertical_idx row.
+ *               MI_VSLASH_EXACT heads also get their vs_bits maps (out->vs_bits
+ *               must then be non-NULL).
  *   MI_BSPARSE: block list = bs_block_idx[b, h, a, :bs_block_count], no columns.
  *   MI_ASHAPE : block list = key blocks c <= a holding a sink key (64c <
  *               sink_tokens) or within the local window of some row
@@ -194,6 +209,8 @@ mi_status mi_build_index(const mi_attn_desc* desc, const int32_t* head_pattern,
  * with A(i) from head h's pattern:
  *   MI_VSLASH, MI_BSPARSE: keys j <= i in the listed blocks or listed columns of
  *                          the row's query block (idx);
+ *   MI_VSLASH_EXACT: keys j <= i that are vertical keys or lie on a slash line
+ *              (i - j a slash offset), from idx's lists and vs_bits maps;
  *   MI_ASHAPE: keys j <= i with j < sink_tokens or i - j < local_tokens (idx
  *              holds the block list; edges are masked per element);
  *   MI_DENSE : all keys j <= i (idx not read).

@@ -296,3 +296,59 @@ def test_c5_vertical_slash_1m():
                 idx_blocks=_blocks_to_check(nb, 4, 5), att_heads=[7, 8, 20, 31],
                 att_blocks=_blocks_to_check(nb, 12, 55), dense_heads=[3],
                 dense_blocks=_blocks_to_check(nb, 2, 56))
+
+
+def _exact_rows(q64, k64, v64, scale, a, V, S):
+    """Oracle rows of query block a over the exact Vertical-Slash key sets,
+    one per-row gather each (the independent per-row formulation)."""
+    out = np.empty((64, q64.shape[1]))
+    for r in range(64):
+        i = 64 * a + r
+        out[r], _ = O.attention_row_gather(q64, k64, v64, scale, i, O.vs_exact_allowed(i, V, S))
+    return out
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wname", ["c3local", "c3"])
+def test_exact_vertical_slash_layer(wname):
+    """The element-masked (exact) Vertical-Slash variant at 128K: on the
+    clustered-slash layer (5% of tiles) and on the noise-driven one (99.7% of
+    tiles).  The aligned-tile plan and the exact plan share the estimate; the
+    exact plan's maps equal the selected sets, its index lists equal the
+    aligned ones, and its rows equal attention over the exact key sets."""
+    w = W.WORKLOADS[wname]
+    say(f"exact variant {w.name}: generating")
+    data = W.generate(w)
+    dev = torch.device("cuda")
+    q, k, v = (to_device(data[x], w.dtype, dev) for x in ("q", "k", "v"))
+    kw = dict(last_q=w.last_q, n_vertical=w.n_vertical, n_slash=w.n_slash, force_vertical=w.force_vertical,
+              force_slash=w.force_slash)
+    aligned = mi.LayerPlan(q, k, v, [W.VSLASH] * w.heads_q, **kw)
+    exact = mi.LayerPlan(q, k, v, [W.VSLASH_EXACT] * w.heads_q, **kw)
+    aligned.run()
+    exact.run()
+    torch.cuda.synchronize()
+    say(f"exact variant {w.name}: GPU layers done")
+    assert torch.equal(aligned.vidx, exact.vidx) and torch.equal(aligned.sidx, exact.sidx)
+    assert torch.equal(aligned.index.block_count, exact.index.block_count)
+    assert torch.equal(aligned.index.col_count, exact.index.col_count)
+    nb, g = w.n_blocks, w.group
+    density = float(exact.index.block_count.double().sum()) / (w.heads_q * nb * (nb + 1) / 2)
+    say(f"  tile density {density:.4f}")
+    vidx, sidx = exact.vidx[0].cpu().numpy(), exact.sidx[0].cpu().numpy()
+    bits = exact.index.vs_bits[0].cpu().numpy().view(np.uint32)
+    blocks = _blocks_to_check(nb, 12, 77)
+    for h in range(w.heads_q):
+        Vh, Sh = vidx[h][vidx[h] >= 0], sidx[h][sidx[h] >= 0]
+        for m, members in ((0, Vh), (1, Sh)):
+            got = np.nonzero(np.unpackbits(bits[h, m].view(np.uint8), bitorder="little"))[0] - 64
+            assert np.array_equal(got, members), (h, m)
+    for h in (0, 9, 22, 31):
+        Vh, Sh = vidx[h][vidx[h] >= 0], sidx[h][sidx[h] >= 0]
+        q64, k64, v64 = (W.to_f64(data[x][0, hh], w.dtype) for x, hh in (("q", h), ("k", h // g), ("v", h // g)))
+        for a in blocks:
+            got = exact.o[0, h, 64 * a: 64 * a + 64].double().cpu().numpy()
+            ref = _exact_rows(q64, k64, v64, w.scale, a, Vh, Sh)
+            err = float(np.abs(got - ref).max())
+            assert err < BF16_ATOL, (h, a, err)
+    say(f"exact variant {w.name}: rows match the exact key sets")

@@ -362,3 +362,54 @@ def test_device_schedule_equals_host_schedule(n, hq, hkv, batch, pat):
     items = sorted(x for x in host if x >= 0)
     assert items == list(range(batch * hq * nruns))
 
+
+
+# ----------------------------------------------------------------- exact Vertical-Slash variant
+
+@pytest.mark.parametrize("dtype,d,n,nv,ns", [("bf16", 128, 64 * 23, 40, 90), ("f32", 64, 64 * 13, 30, 50),
+                                              ("bf16", 64, 64 * 9, 600, 600), ("f32", 128, 64 * 7, 5, 3)])
+def test_exact_vertical_slash_attention(dtype, d, n, nv, ns):
+    """MI_VSLASH_EXACT heads: the same tile and column lists as Vertical-Slash
+    heads, membership maps equal to the selected sets, and outputs equal to
+    attention over the exact key sets {j in V} u {i - o : o in S} (j <= i)."""
+    say(f"exact vertical-slash {dtype} d={d} n={n} nv={nv} ns={ns}")
+    hq, hkv = 3, 1
+    _, (q, k, v), (q64, k64, v64) = _inputs(29, hq, hkv, n, d, dtype)
+    pat = [W.VSLASH_EXACT, W.VSLASH, W.VSLASH_EXACT]
+    vidx, sidx, _, _ = mi.vs_estimate(q, k, [0, 1, 2], 64, nv, ns)
+    idx = mi.build_index(q, k, pat, vidx, sidx)
+    o, lse = mi.sparse_prefill(q, k, v, pat, idx)
+    torch.cuda.synchronize()
+    of, lf = f64(o), f64(lse)
+    V, S = vidx.cpu().numpy(), sidx.cpu().numpy()
+    bits = idx.vs_bits.cpu().numpy().view(np.uint32)
+    atol = F32_ATOL if dtype == "f32" else BF16_ATOL
+    nb = n // 64
+    for h in range(hq):
+        Vh, Sh = V[0, h][V[0, h] >= 0], S[0, h][S[0, h] >= 0]
+        for a in range(nb):
+            blocks, cols = gpu_index_lists(idx, 0, h, a)
+            rb = O.vs_block_list(a, Sh)
+            assert np.array_equal(blocks, rb) and np.array_equal(cols, O.vs_column_list(a, Vh, rb)), (h, a)
+        if pat[h] == W.VSLASH_EXACT:
+            for m, members in ((0, Vh), (1, Sh)):
+                got = np.nonzero(np.unpackbits(bits[0, h, m].view(np.uint8), bitorder="little"))[0] - 64
+                assert np.array_equal(got, np.sort(members)), (h, m)
+            res = {a: O.vs_exact_attention(q64[0, h], k64[0, 0], v64[0, 0], d ** -0.5,
+                                           np.arange(64 * a, 64 * a + 64), Vh, Sh) for a in range(nb)}
+        else:
+            res = O.head_attention(q64[0, h], k64[0, 0], v64[0, 0], d ** -0.5, O.HeadIndex(O.VSLASH, n, V=Vh, S=Sh),
+                                   range(nb))
+        for a, (ref, rlse) in res.items():
+            rows = slice(64 * a, 64 * a + 64)
+            assert np.abs(of[0, h, rows] - ref).max() < atol, (h, a, np.abs(of[0, h, rows] - ref).max())
+            assert np.abs(lf[0, h, rows] - rlse).max() < 1e-3, (h, a)
+
+
+def test_exact_vertical_slash_needs_maps():
+    """An exact head without membership maps is rejected before any launch."""
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda")
+    idx = mi.alloc_index(1, 1, 128, 4, 4, "cuda")  # no vs_bits
+    with pytest.raises(mi.MiError) as e:
+        mi.sparse_prefill(q, q, q, [W.VSLASH_EXACT], idx)
+    assert e.value.status == 1 and "vs_bits" in str(e.value)

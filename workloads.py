@@ -22,6 +22,15 @@ Recipe (every array is a pure function of its config and seed):
     and K in float64;
   * plant: m_g = mean of post-rotary Q over the g query heads of a kv group
     and all N positions; K[j] += alpha * m_g for each planted key j;
+  * local bias (the clustered-slash variant only): after the rotary
+    embedding, alpha_local * v_i is added to Q row i and to K row i, with
+    v_i = (cos(w_r i + p_r), sin(w_r i + p_r))_{r < d/2} / sqrt(d/2),
+    w_r = (pi / local_span) (r + 1/2) / (d/2) and phases p_r drawn per kv
+    group (stream t = 3, head 2000 + g); then v_i . v_j = mean_r
+    cos(w_r (i - j)), a term that depends on the offset i - j only, peaks on
+    the diagonal and falls to zero at offset local_span (a sinc-shaped main
+    lobe), so the selected slash lines cluster at small offsets as in local
+    attention;
   * a single rounding to the storage dtype (fp32, or bf16 by
     round-to-nearest-even), after which the arrays are exact in both the
     GPU's storage format and the oracle's float64.
@@ -37,7 +46,7 @@ import numpy as np
 T_Q, T_K, T_V, T_PLANT, T_PATTERN = 0, 1, 2, 3, 4
 
 # Pattern codes; the same numbering is used by the C ABI.
-ASHAPE, VSLASH, BSPARSE, DENSE = 0, 1, 2, 3
+ASHAPE, VSLASH, BSPARSE, DENSE, VSLASH_EXACT = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -54,6 +63,8 @@ class Workload:
     alpha_vertical: float = 0.0
     n_vertical_plants: int = 0
     alpha_block: float = 0.0
+    alpha_local: float = 0.0
+    local_span: int = 8192
     n_hot_blocks: int = 0
     last_q: int = 64
     n_vertical: int = 1000
@@ -100,7 +111,12 @@ C5 = Workload("vs_llama8b_1m_bf16", 1005, 1, 32, 8, 1048576, 128, "bf16", "vs",
               alpha_vertical=3.0, n_vertical_plants=64,
               last_q=64, n_vertical=1000, n_slash=6096)
 
-WORKLOADS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# Clustered-slash variant of the 128K Vertical-Slash layer (not one of the five
+# evaluation shapes): the same shapes and budgets with the local bias, so that
+# the selected slash offsets cluster near the diagonal.
+C3_LOCAL = C3.with_(name="vs_local_128k_bf16", seed=1013, alpha_local=16.0, local_span=8192)
+
+WORKLOADS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c3local": C3_LOCAL}
 
 
 def rng(seed: int, tensor: int, head: int) -> np.random.Generator:
@@ -213,15 +229,27 @@ def generate(w: Workload, with_v: bool = True):
     def one_kv_group(b: int, kvh: int):
         seed = w.seed + 7919 * b
         qsum = np.zeros(d, np.float64)
+        loc = None
+        if w.alpha_local:
+            half = d // 2
+            ph = rng(w.seed, T_PLANT, 2000 + kvh).uniform(0.0, 2.0 * np.pi, half)
+            om = (np.pi / w.local_span) * (np.arange(half) + 0.5) / half
+            ang = np.arange(N, dtype=np.float64)[:, None] * om[None, :] + ph[None, :]
+            loc = w.alpha_local * np.concatenate([np.cos(ang), np.sin(ang)], axis=1) / np.sqrt(half)
+            del ang
         for hq in range(kvh * g, (kvh + 1) * g):
             qh = rng(seed, T_Q, hq).standard_normal((N, d), dtype=np.float32).astype(np.float64)
             qh = _rotate(qh, cos, sin)
+            if loc is not None:
+                qh += loc
             qsum += qh.sum(axis=0)
             q[b, hq] = _store(qh, w.dtype)
             del qh
         m_g = qsum / (g * N)
         kh = rng(seed, T_K, kvh).standard_normal((N, d), dtype=np.float32).astype(np.float64)
         kh = _rotate(kh, cos, sin)
+        if loc is not None:
+            kh += loc
         if w.alpha_vertical and len(plants[kvh]):
             kh[plants[kvh]] += w.alpha_vertical * m_g
         if w.alpha_block and len(hot[kvh]):
