@@ -110,11 +110,12 @@ def test_block_estimate_validation():
                                1 << 40, None) == 2
 
 
-def index_struct(bcap=32, ccap=16, cols=True):
+def index_struct(bcap=32, ccap=16, cols=True, bits=False):
     s = mi.MiIndex()
     s.block_count, s.block_idx = FAKE, FAKE
     s.col_count, s.col_idx = FAKE, (FAKE if cols else None)
     s.block_cap, s.col_cap = bcap, ccap
+    s.vs_bits = FAKE if bits else None
     return s
 
 
@@ -139,6 +140,10 @@ def test_build_index_validation():
     assert call(pat(0, 0, 0, 0), local=0) == 3
     assert call(pat(0, 0, 0, 0), sink=64, local=1000, out=index_struct(bcap=10)) == 3  # 1 + 17 -> 16
     assert call(pat(0, 0, 0, 0), sink=-1) == 3
+    # exact Vertical-Slash heads: the same lists plus membership maps
+    assert call(pat(4, 1, 1, 1), out=index_struct(bits=False)) == 1
+    assert call(pat(4, 4, 4, 4), out=index_struct(bcap=15, bits=True)) == 3
+    assert call(pat(4, 1, 1, 5)) == 7
 
 
 def test_sparse_prefill_validation():
@@ -155,6 +160,8 @@ def test_sparse_prefill_validation():
     assert call(pat(1, 3, 3, 3), index_struct(cols=False)) == 1
     assert call(pat(0, 3, 3, 3), index_struct(), local=0) == 3
     assert call(pat(5, 3, 3, 3), index_struct()) == 7
+    assert call(pat(4, 3, 3, 3), index_struct()) == 1       # exact heads need the maps
+    assert call(pat(4, 3, 3, 3), index_struct(cols=False, bits=True)) == 1
     assert call(None, o=None) == 1
     assert call(None, o=FAKE + 8) == 2
 
@@ -226,3 +233,23 @@ def test_attention_schedule_groups_heads_of_one_kv_group_and_class():
     # dense comparator: every head in one class
     n2 = l.mi_attn_schedule(ctypes.byref(d), None, 128, 256, 8, None, 0)
     assert n2 == B * Hq * nruns
+
+
+def test_noalloc_prefill_validation():
+    """mi_sparse_prefill_noalloc validates like mi_sparse_prefill and rejects
+    layers whose item schedule exceeds its built-in buffer, all before any
+    HIP call."""
+    l = mi.lib()
+    pat = ctypes.cast((ctypes.c_int32 * 4)(1, 1, 1, 1), ctypes.c_void_p)
+    d = desc()
+    assert l.mi_sparse_prefill_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, pat, None, 128, 256, FAKE, None,
+                                       None) == 1
+    assert l.mi_sparse_prefill_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, 128, 256, None, None,
+                                       None) == 1
+    # 256 query heads x 1025 runs of four query blocks > 262144 schedule entries
+    big = desc(heads_q=256, heads_kv=1, seq_len=64 * 4 * 1025, head_dim=64)
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(big, name)[:] = (0, 0, 0)
+    assert l.mi_sparse_prefill_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None, None, 128, 256, FAKE, None,
+                                       None) == 5
+    assert b"built-in buffer" in l.mi_last_error()
