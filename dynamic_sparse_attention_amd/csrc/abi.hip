@@ -148,6 +148,10 @@ mi_status prepare_attn(const mi_attn_desc* d, const void* q, const void* k, cons
     const size_t es = d->dtype == MI_BF16 ? 2 : 4;
     if ((uint64_t)d->k_stride[2] * es * MI_BLOCK >= (1ull << 31) || (uint64_t)d->v_stride[2] * es * MI_BLOCK >= (1ull << 31))
         return fail(MI_ERR_SHAPE, "K/V token strides too large (64 rows must span < 2 GiB)");
+    // the attention addresses a head's K and V rows by 32-bit byte offsets
+    if ((uint64_t)d->k_stride[2] * es * d->seq_len >= (1ull << 32) ||
+        (uint64_t)d->v_stride[2] * es * d->seq_len >= (1ull << 32))
+        return fail(MI_ERR_SHAPE, "K/V token strides too large (seq_len rows must span < 4 GiB)");
     const size_t lds = mi::sparse_attn_lds_bytes(a);
     if (lds > mi::kAttnMaxLds)
         return fail(MI_ERR_SHAPE, "attention needs %zu bytes of LDS (> %zu): seq_len or col_cap too large", lds,

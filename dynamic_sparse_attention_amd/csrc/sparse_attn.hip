@@ -31,11 +31,14 @@
 // at the same time.
 //
 // Staging: K and V rows go from global memory straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane, 1 KiB of consecutive LDS per
-// wave instruction).  K and V each have two buffers.  A group issues copies
-// at the start of its vector phase, while the other group's MFMA phase keeps
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane, 1 KiB of consecutive LDS
+// per wave instruction; the head's rows are one raw buffer, the tile's first
+// row a uniform offset, so a tile copy takes no per-lane address
+// arithmetic).  K and V each have two buffers.  A group issues copies at
+// the start of its vector phase, while the other group's MFMA phase keeps
 // the matrix cores busy: group 1 the copy of K(t+1) in phase 2t, group 0
-// that of V(t) in phase 2t+1; both are waited for at the end of phase 2t+1.  Rows are stored unpadded; 16-byte chunk c of row r sits
+// that of V(t) in phase 2t+1; both are waited for at the end of phase 2t+1.
+// Rows are stored unpadded; 16-byte chunk c of row r sits
 // at position c ^ f(r), f(r) = 4(r%4) + (r/4)%4 (16-chunk rows), so that a K
 // operand read (16 lanes per LDS cycle: 16 consecutive rows, same chunk) and
 // a V transposed read (32 lanes per cycle: 4 rows x 4 chunks) each hit all 64
@@ -162,22 +165,34 @@ __device__ __forceinline__ void issue_rows(char* dst, uint32_t w, const int32_t*
     // step loop (they would not fit in registers and would spill)
     if constexpr (sizeof(T) == 4 && D == 128) asm volatile("" : "+v"(lane));
     const bool col = step_col(w);
-    const char* tile = base + (int64_t)step_kb(w) * 64 * stride_b;
+    // buffer loads: the head's rows as one raw buffer (SGPR descriptor), a
+    // uniform offset for the tile and 32-bit per-lane row offsets
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000);
+    const uint32_t sb = (uint32_t)stride_b;  // the host keeps seq_len * stride below 2^32
+    if (!col) {
+        // a whole tile: loop-invariant lane offsets, the tile in the uniform offset
+        const uint32_t soff = (uint32_t)step_kb(w) * 64u * sb;
 #pragma unroll
-    for (int it = it0; it < it1; ++it) {
-        const int idx = it * kIssueWaves + rank;
-        const int cidx = idx * 64 + lane;
-        const int row = cidx / Layout<T, D>::CPR, pos = cidx % Layout<T, D>::CPR;
-        const int chunk = pos ^ swz<Layout<T, D>::CPR>(row);
-        const char* src;
-        if (!col) {
-            src = tile + (uint32_t)(row * (int32_t)stride_b + chunk * 16);
-        } else {
+        for (int it = it0; it < it1; ++it) {
+            const int idx = it * kIssueWaves + rank;
+            const int cidx = idx * 64 + lane;
+            const int row = cidx / Layout<T, D>::CPR, pos = cidx % Layout<T, D>::CPR;
+            const int chunk = pos ^ swz<Layout<T, D>::CPR>(row);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + idx * 1024), 16,
+                                                     (int)((uint32_t)row * sb + chunk * 16), (int)soff, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int it = it0; it < it1; ++it) {
+            const int idx = it * kIssueWaves + rank;
+            const int cidx = idx * 64 + lane;
+            const int row = cidx / Layout<T, D>::CPR, pos = cidx % Layout<T, D>::CPR;
+            const int chunk = pos ^ swz<Layout<T, D>::CPR>(row);
             const int tok = tok_src[row];
             if (tok_dst && pos == 0) tok_dst[row] = tok;
-            src = base + (int64_t)max(tok, 0) * stride_b + chunk * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + idx * 1024), 16,
+                                                     (int)((uint32_t)max(tok, 0) * sb + chunk * 16), 0, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + idx * 1024), 16, 0, 0);
     }
 }
 
@@ -286,23 +301,39 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 //       (base + 8sec)*ROWB + (vbase ^ (64db + 32sec)),
 //       vbase = (4hl + j)*ROWB + 16(x ^ f(4hl + j)) + 8(qd%2).
 // The XOR constants only touch bits 5..7 (below ROWB); the buffers are
-// 1 KiB aligned.
+// 1 KiB aligned.  Every XORed base is computed once per work item and held
+// in a register (k[ks], v[2 db + sec]): the reads then take the rest of
+// their address (buffer, row, kh) as the instruction's immediate offset,
+// with no address arithmetic in the step loop.
+template <typename T, int D>
 struct LaneBase {
-    int k, v;
+    static constexpr int NK = sizeof(T) == 2 ? D / 16 : 1;
+    static constexpr int NV = sizeof(T) == 2 ? D / 16 : 1;
+    int k[NK], v[NV];
 };
 template <typename T, int D>
-__device__ __forceinline__ LaneBase lane_base(int lane) {
+__device__ __forceinline__ LaneBase<T, D> lane_base(int lane) {
     typedef Layout<T, D> Ly;
     const int rl = lane & 31, hl = lane >> 5;
-    LaneBase b;
+    LaneBase<T, D> b;
     if constexpr (sizeof(T) == 2) {
-        b.k = rl * Ly::ROWB + 16 * (hl ^ swz<Ly::CPR>(rl));
+        const int kb = rl * Ly::ROWB + 16 * (hl ^ swz<Ly::CPR>(rl));
         const int g16 = (lane >> 4) & 1, s = lane & 15, j = s >> 2, qd = s & 3;
         const int x = 2 * g16 + (qd >> 1);
-        b.v = (4 * hl + j) * Ly::ROWB + 16 * (x ^ swz<Ly::CPR>(4 * hl + j)) + 8 * (qd & 1);
+        const int vb = (4 * hl + j) * Ly::ROWB + 16 * (x ^ swz<Ly::CPR>(4 * hl + j)) + 8 * (qd & 1);
+#pragma unroll
+        for (int i = 0; i < LaneBase<T, D>::NK; ++i) {
+            b.k[i] = kb ^ (32 * i);
+            asm volatile("" : "+v"(b.k[i]));  // materialised once, not recomputed in the loop
+        }
+#pragma unroll
+        for (int i = 0; i < LaneBase<T, D>::NV; ++i) {
+            b.v[i] = vb ^ (64 * (i >> 1) + 32 * (i & 1));
+            asm volatile("" : "+v"(b.v[i]));
+        }
     } else {
-        b.k = rl * Ly::ROWB;
-        b.v = 0;
+        b.k[0] = rl * Ly::ROWB;
+        b.v[0] = 0;
     }
     return b;
 }
@@ -310,15 +341,15 @@ __device__ __forceinline__ LaneBase lane_base(int lane) {
 // K operand (8 elements of key row kh*32 + rl, slots 16 ks + 8 hl ..) from
 // the K buffer `kbuf`.
 template <int D>
-__device__ __forceinline__ bf16x8 k_frag_bf16(const char* kbuf, const LaneBase& lb, int kh, int ks) {
-    const char* a = kbuf + ((lb.k ^ (32 * ks)) + kh * 32 * Layout<uint16_t, D>::ROWB);
+__device__ __forceinline__ bf16x8 k_frag_bf16(const char* kbuf, const LaneBase<uint16_t, D>& lb, int kh, int ks) {
+    const char* a = kbuf + (lb.k[ks] + kh * 32 * Layout<uint16_t, D>::ROWB);
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
 }
 template <int D>
-__device__ __forceinline__ f32x8 k_frag_f32(const char* kbuf, const LaneBase& lb, int kh, int ks) {
+__device__ __forceinline__ f32x8 k_frag_f32(const char* kbuf, const LaneBase<float, D>& lb, int kh, int ks) {
     typedef Layout<float, D> Ly;
     const int rl = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
-    const char* row = kbuf + kh * 32 * Ly::ROWB + lb.k;
+    const char* row = kbuf + kh * 32 * Ly::ROWB + lb.k[0];
     const int f = swz<Ly::CPR>(rl);
     const f32x4 a = *reinterpret_cast<const f32x4*>(row + (((4 * ks + 2 * hl) ^ f) * 16));
     const f32x4 b = *reinterpret_cast<const f32x4*>(row + (((4 * ks + 2 * hl + 1) ^ f) * 16));
@@ -329,17 +360,17 @@ __device__ __forceinline__ f32x8 k_frag_f32(const char* kbuf, const LaneBase& lb
 // `vbuf`: lane (d = 32 db + l%32, half hl) gets keys base+4hl+{0..3} and
 // base+8+4hl+{0..3}.
 template <int D>
-__device__ __forceinline__ bf16x8 v_frag_bf16(const char* vbuf, const LaneBase& lb, int db, int base) {
+__device__ __forceinline__ bf16x8 v_frag_bf16(const char* vbuf, const LaneBase<uint16_t, D>& lb, int db, int base) {
     constexpr int RB = Layout<uint16_t, D>::ROWB;
-    const char* p0 = vbuf + ((lb.v ^ (64 * db)) + base * RB);
-    const char* p1 = vbuf + ((lb.v ^ (64 * db + 32)) + (base + 8) * RB);
+    const char* p0 = vbuf + (lb.v[2 * db] + base * RB);
+    const char* p1 = vbuf + (lb.v[2 * db + 1] + (base + 8) * RB);
     const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
     const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
     const i16x8 r = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     return __builtin_bit_cast(bf16x8, r);
 }
 template <int D>
-__device__ __forceinline__ f32x8 v_frag_f32(const char* vbuf, const LaneBase&, int db, int base) {
+__device__ __forceinline__ f32x8 v_frag_f32(const char* vbuf, const LaneBase<float, D>&, int db, int base) {
     typedef Layout<float, D> Ly;
     const int rl = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
     const int d = db * 32 + rl;
@@ -354,12 +385,12 @@ __device__ __forceinline__ f32x8 v_frag_f32(const char* vbuf, const LaneBase&, i
 }
 
 template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::frag k_frag(const char* kbuf, const LaneBase& lb, int kh, int ks) {
+__device__ __forceinline__ typename Elem<T>::frag k_frag(const char* kbuf, const LaneBase<T, D>& lb, int kh, int ks) {
     if constexpr (sizeof(T) == 2) return k_frag_bf16<D>(kbuf, lb, kh, ks);
     else return k_frag_f32<D>(kbuf, lb, kh, ks);
 }
 template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::frag v_frag(const char* vbuf, const LaneBase& lb, int db, int base) {
+__device__ __forceinline__ typename Elem<T>::frag v_frag(const char* vbuf, const LaneBase<T, D>& lb, int db, int base) {
     if constexpr (sizeof(T) == 2) return v_frag_bf16<D>(vbuf, lb, db, base);
     else return v_frag_f32<D>(vbuf, lb, db, base);
 }
@@ -425,7 +456,7 @@ struct QOperand {
 
 // S^T = K . Q^T for one step (the two 32-key halves interleaved).
 template <typename T, int D>
-__device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, const LaneBase& lb,
+__device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, const LaneBase<T, D>& lb,
                                           const QOperand<T, D>& qf) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -578,27 +609,9 @@ __device__ __forceinline__ bool raise_max(RowState<T, D>& rs, float mx, float& a
     return __ballot(raise) != 0;
 }
 
-// Probabilities of one 32-key half of a step against the running max, as
-// P.V operands; returns their fp32 sum.
-template <typename T>
-__device__ __forceinline__ float probs_half(typename Elem<T>::frag (&pf)[2], const f32x16& s, float m_use,
-                                            float c) {
-    typedef typename Elem<T>::frag Frag;
-    float sum = 0.f;
-    f32x16 pv;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        pv[e] = fast_exp2(fmaf(s[e], c, -m_use));
-        sum += pv[e];
-    }
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) pf[pp] = make_p_frag(pv, 8 * pp, (Frag*)nullptr);
-    return sum;
-}
-
 // O^T += V^T . P^T over 16-key chunks (half kh, part pp).
 template <typename T, int D>
-__device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vbuf, const LaneBase& lb,
+__device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vbuf, const LaneBase<T, D>& lb,
                                               const typename Elem<T>::frag (&pf)[2][2]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -621,6 +634,28 @@ __device__ __forceinline__ void pv_accumulate(RowState<T, D>& rs, const char* vb
     }
 }
 
+// bf16: the probabilities of a step as P.V operands: pf[kh][pp] holds keys
+// 16 pp .. 16 pp + 15 of half kh (8 per lane) as bf16 pairs; returns their
+// fp32 sum (before rounding).
+__device__ __forceinline__ float probs_bf16(bf16x8 (&pf)[2][2], const f32x16 (&s)[2], float m_use, float c) {
+    float sum = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            u32x4 u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(s[kh][8 * pp + 2 * e], c, -m_use));
+                const float p1 = fast_exp2(fmaf(s[kh][8 * pp + 2 * e + 1], c, -m_use));
+                u[e] = pack_bf16x2(p0, p1);
+                sum += p0 + p1;
+            }
+            pf[kh][pp] = __builtin_bit_cast(bf16x8, u);
+        }
+    return sum;
+}
+
 // fp32: the probabilities overwrite the scores (an fp32 P operand is the
 // score registers themselves); returns their sum.
 __device__ __forceinline__ float probs_in_place(f32x16 (&s)[2], float m_use, float c) {
@@ -638,7 +673,7 @@ __device__ __forceinline__ float probs_in_place(f32x16 (&s)[2], float m_use, flo
 // fp32 O^T += V^T . P^T with P read straight from the score registers
 // (16-key chunk pp of half kh is elements 8 pp .. 8 pp + 7 of s[kh]).
 template <int D>
-__device__ __forceinline__ void pv_accumulate_f32(RowState<float, D>& rs, const char* vbuf, const LaneBase& lb,
+__device__ __forceinline__ void pv_accumulate_f32(RowState<float, D>& rs, const char* vbuf, const LaneBase<float, D>& lb,
                                                   const f32x16 (&s)[2]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -652,46 +687,6 @@ __device__ __forceinline__ void pv_accumulate_f32(RowState<float, D>& rs, const 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-}
-
-// Between phases a wavefront carries either its scores or its P operands,
-// never both: P is parked in the score registers.
-__device__ __forceinline__ void park_p(f32x16 (&s)[2], const bf16x8 (&pf)[2][2]) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const f32x4 w = __builtin_bit_cast(f32x4, pf[kh][pp]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[0][(kh * 2 + pp) * 4 + e] = w[e];
-        }
-}
-__device__ __forceinline__ void unpark_p(bf16x8 (&pf)[2][2], const f32x16 (&s)[2]) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            f32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = s[0][(kh * 2 + pp) * 4 + e];
-            pf[kh][pp] = __builtin_bit_cast(bf16x8, w);
-        }
-}
-__device__ __forceinline__ void park_p(f32x16 (&s)[2], const f32x8 (&pf)[2][2]) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[kh][pp * 8 + e] = pf[kh][pp][e];
-}
-__device__ __forceinline__ void unpark_p(f32x8 (&pf)[2][2], const f32x16 (&s)[2]) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[kh][pp][e] = s[kh][pp * 8 + e];
 }
 
 // Barrier that does not wait for outstanding global->LDS copies.
@@ -765,7 +760,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
 
     QOperand<T, D> qf;
     qf.init(qbase + (int64_t)i_row * p.qs2 + 8 * hl, active);
-    const LaneBase lb = lane_base<T, D>(lane);
+    const LaneBase<T, D> lb = lane_base<T, D>(lane);
 
     RowState<T, D> rs;
 #pragma unroll
@@ -776,7 +771,11 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     rs.l_part = 0.f;
 
     auto needs = [&](uint32_t w) { return active && w != kNoStep && ((step_need(w) >> blk) & 1); };
-    f32x16 s[2];  // scores of the current step, or its parked P operands
+    // The scores of a step live from its MFMA phase to its vector phase
+    // only (fp32: then its probabilities, in place, up to the next MFMA
+    // phase); bf16 P operands are carried to the next MFMA phase in pfr.
+    Frag pfr[2][2];
+    f32x16 s_keep[2];  // the scores (fp32: then the parked probabilities)
     float alpha = 1.f;     // accumulator factor of the last vector phase
     bool rescale = false;  // some row of the wavefront raised its max
 
@@ -787,80 +786,102 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     // start of phase 2t+1 (the buffers' last readers finished in phase
     // 2t-1); every wave waits for its own copies at the end of phase 2t+1.
     uint32_t wprev = kNoStep, wcur = fetch(0), wnext = fetch(1);
-    // one step; the loop below unrolls it twice so that every buffer is a
-    // fixed LDS object in each copy
-    auto step = [&](int t, char* kcur, char* knext, char* vcur, const char* vprev, const int32_t* cpcur,
-                    int32_t* cpnext) __attribute__((always_inline)) {
-        const bool pv_need = needs(wprev);
-        const bool s_need = needs(wcur);
+    // M(t) on this wavefront: P.V of step t-1 (V buffer vprev), then S of
+    // step t (K buffer kcur) and its mask.
+    auto m_phase = [&](const char* kcur, const char* vprev, const int32_t* cpcur, bool pv_need, bool s_need,
+                       f32x16 (&s)[2]) __attribute__((always_inline)) {
+        if (pv_need) {
+            if (rescale) {
 #pragma unroll
-        for (int ph = 0; ph < 2; ++ph) {
-            if (ph == grp) {
-                // M(t): P.V of step t-1, then S of step t.  Opaque lane bases
-                // keep the operand addresses from being hoisted out of the loop.
-                LaneBase lbo = lb;
-                asm volatile("" : "+v"(lbo.k), "+v"(lbo.v));
-                if (pv_need) {
-                    if (rescale) {
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e) rs.oacc[db][e] *= alpha;
-                    }
-                    if constexpr (sizeof(T) == 2) {
-                        Frag pf[2][2];
-                        unpark_p(pf, s);
-                        pv_accumulate<T, D>(rs, vprev, lbo, pf);
-                    } else {
-                        pv_accumulate_f32<D>(rs, vprev, lbo, s);
-                    }
-                }
-                if (s_need) {
-                    s_compute<T, D>(s, kcur, lbo, qf);
-                    mask_scores<EXACT>(s, step_mode<EXACT>(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row,
-                                ex_bits, my_a * 64 + (wave & 1) * 32);
-                }
-            } else {
-                // Vector phase: V(t-1) for group 1, V(t) for group 0.  The
-                // group entering it first issues one of the copies, while the
-                // other group keeps the matrix cores busy: K(t+1) by group 1
-                // in phase 2t, V(t) by group 0 in phase 2t+1.
-                constexpr int NI = Ly::CPR / kIssueWaves;
-                if (ph == 0) {
-                    if (wnext != kNoStep)
-                        issue_rows<T, D>(knext, wnext, colsl + step_blk(wnext) * cstride + step_kb(wnext), cpnext,
-                                         kbase, kstride, wave & 3, 0, NI);
-                } else {
-                    if (wcur != kNoStep) issue_rows<T, D>(vcur, wcur, cpcur, nullptr, vbase, vstride, wave & 3, 0, NI);
-                }
-                if (grp == 1 ? pv_need : s_need) {
-                    rescale = raise_max<T, D>(rs, row_max(s, p.c), alpha);
-                    const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
-                    if constexpr (sizeof(T) == 2) {
-                        Frag pf[2][2];
-                        rs.l_part += probs_half<T>(pf[0], s[0], m_use, p.c) + probs_half<T>(pf[1], s[1], m_use, p.c);
-                        park_p(s, pf);
-                    } else {
-                        rs.l_part += probs_in_place(s, m_use, p.c);
-                    }
-                }
+                    for (int e = 0; e < 16; ++e) rs.oacc[db][e] *= alpha;
             }
-            if (ph == 0) phase_barrier();
+            if constexpr (sizeof(T) == 2) {
+                pv_accumulate<T, D>(rs, vprev, lb, pfr);
+            } else {
+                pv_accumulate_f32<D>(rs, vprev, lb, s);
+            }
         }
-        if (wcur == kNoStep) return false;
-        __syncthreads();  // K(t+1) and V(t) have landed; phase 2t+2 begins
+        if (s_need) {
+            s_compute<T, D>(s, kcur, lb, qf);
+            mask_scores<EXACT>(s, step_mode<EXACT>(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row, ex_bits,
+                               my_a * 64 + (wave & 1) * 32);
+        }
+    };
+    // Vector phase on this wavefront: row max, running-max update,
+    // probabilities (parked as P operands over the scores).
+    auto v_phase = [&](bool need, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        if (need) {
+            rescale = raise_max<T, D>(rs, row_max(s, p.c), alpha);
+            const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
+            if constexpr (sizeof(T) == 2) {
+                rs.l_part += probs_bf16(pfr, s, m_use, p.c);
+            } else {
+                rs.l_part += probs_in_place(s, m_use, p.c);
+            }
+        }
+    };
+    constexpr int NI = Ly::CPR / kIssueWaves;
+    // Each group runs its steps in a loop of its own (the two loops meet at
+    // the same barriers): phase 2t: group 0 runs M(t) while group 1 issues
+    // the copy of K(t+1) and runs V(t-1); phase 2t+1: group 1 runs M(t)
+    // while group 0 issues the copy of V(t) and runs V(t).  K(t) sits in K
+    // buffer t%2, V(t) in V buffer t%2; the loops unroll two steps so that
+    // every buffer is a fixed LDS object in each copy.  Every wave waits for
+    // its own copies at the end of phase 2t+1.  Group 1's loop is rotated
+    // (M(t), barrier, copy of K(t+2), V(t)) so that a step's scores never
+    // cross an iteration.
+    auto advance = [&](int t) __attribute__((always_inline)) {
         wprev = wcur;
         wcur = wnext;
         wnext = fetch(t + 2);
+    };
+    // fp32 keeps its probabilities in the score registers until the next
+    // MFMA phase (s_keep: they cross the iteration there); bf16 scores are
+    // local to a step (sl).
+    auto step0 = [&](int t, const char* kcur, char* vcur, const char* vprev, const int32_t* cpcur)
+        __attribute__((always_inline)) {
+        const bool pv_need = needs(wprev), s_need = needs(wcur);
+        f32x16 (&s)[2] = s_keep;
+        m_phase(kcur, vprev, cpcur, pv_need, s_need, s);
+        phase_barrier();
+        if (wcur != kNoStep) issue_rows<T, D>(vcur, wcur, cpcur, nullptr, vbase, vstride, wave & 3, 0, NI);
+        v_phase(s_need, s);
+        if (wcur == kNoStep) return false;
+        __syncthreads();  // K(t+1) and V(t) have landed; phase 2t+2 begins
+        advance(t);
+        return true;
+    };
+    auto step1 = [&](int t, const char* kcur, char* knext, const char* vprev, const int32_t* cpcur, int32_t* cpnext)
+        __attribute__((always_inline)) {
+        const bool pv_need = needs(wprev), s_need = needs(wcur);
+        f32x16 (&s)[2] = s_keep;
+        if (wnext != kNoStep)
+            issue_rows<T, D>(knext, wnext, colsl + step_blk(wnext) * cstride + step_kb(wnext), cpnext, kbase,
+                             kstride, wave & 3, 0, NI);
+        v_phase(pv_need, s);
+        phase_barrier();
+        m_phase(kcur, vprev, cpcur, pv_need, s_need, s);
+        if (wcur == kNoStep) return false;
+        __syncthreads();
+        advance(t);
         return true;
     };
     if (wcur != kNoStep && grp == 1)
         issue_rows<T, D>(kbuf0, wcur, colsl + step_blk(wcur) * cstride + step_kb(wcur), cpos0, kbase, kstride,
-                         wave & 3, 0, Ly::CPR / kIssueWaves);
+                         wave & 3, 0, NI);
     __syncthreads();
-    for (int t = 0;; t += 2) {
-        if (!step(t, kbuf0, kbuf1, vbuf0, vbuf1, cpos0, cpos1)) break;
-        if (!step(t + 1, kbuf1, kbuf0, vbuf1, vbuf0, cpos1, cpos0)) break;
+    if (grp == 0) {
+        for (int t = 0;; t += 2) {
+            if (!step0(t, kbuf0, vbuf0, vbuf1, cpos0)) break;
+            if (!step0(t + 1, kbuf1, vbuf1, vbuf0, cpos1)) break;
+        }
+    } else {
+        for (int t = 0;; t += 2) {
+            if (!step1(t, kbuf0, kbuf1, vbuf1, cpos0, cpos1)) break;
+            if (!step1(t + 1, kbuf1, kbuf0, vbuf0, cpos1, cpos0)) break;
+        }
     }
 
     if (!active) return;

@@ -193,6 +193,9 @@ def test_sparse_prefill_rejects_oversized_lds_and_strides():
     # a token stride of 2^25 elements: 64 rows span 4 GiB
     wide = desc(k_stride=(1 << 40, 1 << 32, 1 << 25))
     assert call(wide, index_struct(), "strides too large") == 2
+    # 256 rows of 16 MiB: a head's rows span 4 GiB (32-bit row offsets)
+    far = desc(seq_len=256, v_stride=(1 << 40, 1 << 33, 1 << 23))
+    assert call(far, index_struct(bcap=4, ccap=4), "span < 4 GiB") == 2
 
 
 
