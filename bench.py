@@ -30,6 +30,7 @@ METRIC = "ms/layer sparse prefill attention at 128K & 1M; achieved MFMA TFLOP/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
+W_VS = 1  # Vertical-Slash pattern code
 
 
 def log(*a):
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal comparator")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token secondary measurement")
+    ap.add_argument("--no-gather", action="store_true", help="skip the isolated column-gather rate")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact (element-masked) Vertical-Slash variant and the clustered-slash layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -67,20 +69,33 @@ def calibrate_copy():
                                          "bytes_written_per_launch": 1 << 30}}))
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on this workload with the current kernel source;
-    otherwise None (the counters describe another kernel)."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "sparse_attn_vs128k_hbm.json")
-    if not os.path.exists(path):
+def profile_record(workload: str):
+    """The committed rocprofv3 record of this workload's layer if it was taken
+    on the current kernel sources, else None."""
+    from dynamic_sparse_attention_amd import profile_tables
+    return profile_tables.current_record(workload)
+
+
+def measured_traffic(rec):
+    """HBM bytes per attention launch (scaled FETCH_SIZE + WRITE_SIZE) from a
+    current profile record, else None."""
+    if rec is None:
         return None
-    rec = json.load(open(path))
-    csrc = os.path.join(ROOT, "dynamic_sparse_attention_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("sparse_attn.hip", "mi_device.h"))
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+    for r in rec["kernels"]:
+        if r["kernel"].startswith("sparse_attn_kernel") and "measured_bytes" in r:
+            return float(r["measured_bytes"])
+    return None
+
+
+def kernels_hbm(rec):
+    """Per-kernel HBM rate and share of the 8 TB/s peak from a current profile
+    record (measured bytes from the counters, algorithmic bytes from the
+    shapes), or None when the record is missing or describes older kernels."""
+    if rec is None:
         return None
-    return float(rec["traffic_bytes_per_launch"])
+    keys = ("avg_us", "measured_GBps", "measured_pct_hbm", "algorithmic_GBps", "algorithmic_pct_hbm",
+            "clock_MHz", "mfma_busy")
+    return {r["kernel"]: {k: r[k] for k in keys if k in r} for r in rec["kernels"]}
 
 
 def index_work(plan, d):
@@ -280,6 +295,91 @@ def measure(w, steps, warmup, dense, keep=False, exact=False, data=None):
     return res, plan, data
 
 
+def gather_rate(q, k, v, w, n_vertical=1000):
+    """The column gather on its own: the same Q/K/V with a column-only index
+    (slash set {0}: each query block computes its diagonal tile only, plus
+    up to n_vertical gathered key columns, seeded and spread over the
+    sequence).  Bytes are the gathered K and V rows (2 * d * elem per column
+    per query block); the diagonal tiles' share of the time is measured with
+    no columns at all and taken out."""
+    import torch
+    import dynamic_sparse_attention_amd as mi
+    B, Hq, N, d = q.shape
+    es = q.element_size()
+    dev = q.device
+    g = np.random.default_rng(77)
+    vidx = torch.empty((B, Hq, n_vertical), dtype=torch.int32)
+    for b in range(B):
+        for h in range(Hq):
+            vidx[b, h] = torch.from_numpy(np.sort(np.concatenate(
+                [[0], g.choice(np.arange(1, N), n_vertical - 1, replace=False)])).astype(np.int32))
+    vidx = vidx.to(dev)
+    sidx = torch.zeros((B, Hq, 1), dtype=torch.int32, device=dev)
+    pats = [W_VS] * Hq
+    idx = mi.build_index(q, k, pats, vidx, sidx)
+    none = mi.build_index(q, k, pats, vidx[..., :1], sidx)  # key 0 only: in the diagonal tile of block 0
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def timed(ix):
+        mi.sparse_prefill(q, k, v, pats, ix, out=out, return_lse=False)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mi.sparse_prefill(q, k, v, pats, ix, out=out, return_lse=False)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms = timed(idx)
+    base = timed(none)
+    cols = int(idx.col_count.to(torch.int64).sum())
+    byts = cols * 2 * d * es
+    rate = byts / max(ms - base, 1e-6) / 1e6
+    return {"columns": cols, "bytes": byts, "attention_ms": round(ms, 3), "diagonal_only_ms": round(base, 3),
+            "gather_GBps": round(rate, 1), "frac_of_hbm_peak": round(rate / PEAK_HBM_GBS, 4),
+            "note": "gathered K/V rows per query block over the time the columns add; rows are served "
+                    "from L2/MALL as much as from HBM"}
+
+
+def sampled_parity(plan, w, data, n_items=8):
+    """Attention rows of the plan (relaunched on its index, since the dense
+    comparator shares the output buffer) against the oracle fed the GPU's
+    own index, on seeded (head, query block) samples (the oracle at full size
+    would take hours): the largest absolute difference."""
+    import torch
+    import workloads as W
+    from oracle import minference_oracle as O
+    plan.attention()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    nb, g = w.n_blocks, w.group
+    worst = 0.0
+    items = []
+    for _ in range(n_items):
+        h = int(rng.integers(w.heads_q))
+        a = int(rng.choice([0, nb - 1, int(rng.integers(nb))]))
+        items.append((h, a))
+    for h, a in items:
+        bc = int(plan.index.block_count[0, h, a])
+        blocks = plan.index.block_idx[0, h, a, :bc].cpu().numpy()
+        cc = int(plan.index.col_count[0, h, a])
+        cols = plan.index.col_idx[0, h, a, :cc].cpu().numpy() if plan.pat[h] == W.VSLASH else []
+        q64, k64, v64 = (W.to_f64(data[x][0, hh], w.dtype) for x, hh in (("q", h), ("k", h // g), ("v", h // g)))
+        if plan.pat[h] == W.ASHAPE:
+            ref, _ = O.ashape_attention(q64, k64, v64, w.scale, np.arange(64 * a, 64 * a + 64), w.sink, w.local)
+        else:
+            ref, _ = O.attention_from_index(q64, k64, v64, w.scale, a, blocks, cols)
+        got = plan.o[0, h, 64 * a: 64 * a + 64].double().cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref).max()))
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+    return {"attention_max_abs": worst, "tolerance": tol, "items": len(items), "ok": worst < tol,
+            "reference": "fp64 oracle fed the GPU's index, seeded (head, query block) samples"}
+
+
 def mi_layer_plan(q, k, v, pats, w):
     import dynamic_sparse_attention_amd as mi
     return mi.LayerPlan(q, k, v, pats, last_q=w.last_q, n_vertical=w.n_vertical, n_slash=w.n_slash,
@@ -331,6 +431,7 @@ def main():
     d = w.head_dim
     achieved = r["flop"] / (r["att_ms"] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    prof = profile_record(w.name)
     out = {
         "metric": METRIC,
         "value": round(r["ms_step"], 4),
@@ -351,7 +452,7 @@ def main():
                    "top_blocks": w.top_blocks, "sink": w.sink, "local": w.local},
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(prof),
                      "flop_per_launch": r["flop"]},
         "kernels_ms": {"estimate": round(r["est_ms"], 4), "build_index": round(r["idx_ms"], 4),
                        "attention": round(r["att_ms"], 4)},
@@ -360,12 +461,19 @@ def main():
         "index": {"tiles": r["tiles"], "columns": r["cols"],
                   "tile_density": round(r["tiles"] / r["causal_tiles"], 4)},
         "exact_pattern": exact_summary(r, d),
+        "kernels_hbm": kernels_hbm(prof),
     }
     if "dense" in r:
         out["dense_comparator"] = r["dense"]
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, data, plan, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        log("[bench] sampled parity against the oracle")
+        out["parity"] = sampled_parity(plan, w, data)
+    if not args.no_gather and w.seq_len >= 65536 and w.dtype == "bf16":
+        log("[bench] column gather rate")
+        out["gather"] = gather_rate(plan.q, plan.k, plan.v, w)
     if not args.no_exact and any(p == W.VSLASH for p in plan.pat):
         # the same layer with the Vertical-Slash heads element-masked to their
         # exact key sets: attention time on the same estimate and index lists
