@@ -5,12 +5,16 @@
 //
 //   1. pool:   fp32 means of the 64 rows of every query block of the listed
 //              heads and every key block of their kv heads (HBM-bound read of
-//              Q and K once);
-//   2. scores: z[a][c] = scale * Qbar_a . Kbar_c for c <= a, 64x64 tiles of
-//              the lower triangle, fp32 FMA from LDS;
+//              Q and K once, 16-byte loads);
+//   2. scores: z[a][c] = scale * Qbar_a . Kbar_c for c <= a, fp32 FMA from
+//              LDS;
 //   3. select: per query block a, softmax over c <= a (the block-level
-//              attention weights, written out), then the exact top-k with
-//              blocks 0 and a forced (mi_select.h).
+//              attention weights, formed in registers or LDS and written out
+//              only when the caller asks for them), then the exact top-k by
+//              weight with blocks 0 and a forced (mi_select.h).
+// Rows of up to 512 blocks fuse 2 and 3 (bs_fused: the scores stay in LDS);
+// longer rows keep the scores in the workspace between two kernels.
+#include "mi_device.h"
 #include "mi_internal.h"
 #include "mi_select.h"
 
@@ -35,35 +39,74 @@ struct BsP {
     int32_t* block_count;  // [B, Hq, nb]
 };
 
-template <typename T>
-__device__ __forceinline__ float ld(const T* p);
-template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+// One workgroup per (pooled row set, block): lane group g of D/8 lanes
+// reads rows g, g + G, ... of the block (G = 256 / (D/8) row groups), each
+// lane 8 consecutive elements (16-byte loads for bf16), then the G partial
+// sums of each column are added in group order through LDS.
+constexpr int kPoolNT = 256;
 
-// One workgroup per (pooled row set, block); thread d sums column d.
 template <typename T>
-__global__ void __launch_bounds__(128) bs_pool(BsP p) {
+__device__ __forceinline__ void load8(const T* src, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* src, float (&x)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* src, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kPoolNT) bs_pool(BsP p) {
+    constexpr int LPR = D / 8;            // lanes per row
+    constexpr int G = kPoolNT / LPR;      // row groups
+    __shared__ float part[G][D + 1];
     const int a = blockIdx.x % p.nb;
     const int r = blockIdx.x / p.nb;  // [0, B*n_heads) queries, then [.., + B*n_kv) keys
-    const int d = threadIdx.x;
-    if (d >= p.D) return;
     const T* src;
     float* dst;
+    int64_t rs;
     if (r < p.B * p.n_heads) {
         const int b = r / p.n_heads, li = r % p.n_heads;
         src = reinterpret_cast<const T*>(p.q) + b * p.qs0 + p.heads[li] * p.qs1 + (int64_t)a * 64 * p.qs2;
-        dst = p.qbar + ((int64_t)r * p.nb + a) * p.D;
-        float acc = 0.f;
-        for (int i = 0; i < 64; ++i) acc += ld(src + (int64_t)i * p.qs2 + d);
-        dst[d] = acc * (1.0f / 64.0f);
+        dst = p.qbar + ((int64_t)r * p.nb + a) * D;
+        rs = p.qs2;
     } else {
         const int rk = r - p.B * p.n_heads;
         const int b = rk / p.n_kv, ki = rk % p.n_kv;
         src = reinterpret_cast<const T*>(p.k) + b * p.ks0 + p.kvlist[ki] * p.ks1 + (int64_t)a * 64 * p.ks2;
-        dst = p.kbar + ((int64_t)rk * p.nb + a) * p.D;
-        float acc = 0.f;
-        for (int i = 0; i < 64; ++i) acc += ld(src + (int64_t)i * p.ks2 + d);
-        dst[d] = acc * (1.0f / 64.0f);
+        dst = p.kbar + ((int64_t)rk * p.nb + a) * D;
+        rs = p.ks2;
+    }
+    const int g = threadIdx.x / LPR, c8 = threadIdx.x % LPR;
+    float x[64 / G][8];
+#pragma unroll
+    for (int u = 0; u < 64 / G; ++u) load8<T>(src + (int64_t)(g + G * u) * rs + 8 * c8, x[u]);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        acc[i] = x[0][i];
+#pragma unroll
+        for (int u = 1; u < 64 / G; ++u) acc[i] += x[u][i];
+        part[g][8 * c8 + i] = acc[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < G; ++q) sum += part[q][threadIdx.x];
+        dst[threadIdx.x] = sum * (1.0f / 64.0f);
     }
 }
 
@@ -135,8 +178,17 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
     return r;
 }
 
-// Per (batch, listed head, query block a): softmax of z[a][0..a], written
-// back as w (zeros for c > a), then top-k with blocks 0 and a forced.
+// Selection key of block c of row a: the weight's order key, forced blocks
+// 0 and a above every weight.
+__device__ __forceinline__ uint32_t block_key(float w, int c, int a) {
+    return (c == 0 || c == a) ? kForcedKey : order_key(w);
+}
+
+// Per (batch, listed head, query block a), rows longer than the wavefront
+// form holds: the row staged in LDS, its softmax w over c <= a, top-k by w
+// with blocks 0 and a forced, and (WEIGHTS) w written back over z (zeros for
+// c > a).
+template <bool WEIGHTS>
 __global__ void __launch_bounds__(kSelNT) bs_select(BsP p) {
     extern __shared__ float row[];  // nb floats
     __shared__ SelectSmem sm;
@@ -167,66 +219,31 @@ __global__ void __launch_bounds__(kSelNT) bs_select(BsP p) {
             wv = row[c] / sum;
             row[c] = wv;
         }
-        W[c] = wv;
+        if constexpr (WEIGHTS) W[c] = wv;
     }
     __syncthreads();
-    auto key = [&](int c) -> uint32_t { return (c == 0 || c == a) ? kForcedKey : order_key(row[c]); };
+    auto key = [&](int c) -> uint32_t { return block_key(row[c], c, a); };
     const int k = min(p.top, n);
     int32_t* out = p.block_idx + (((int64_t)b * p.Hq + h) * p.nb + a) * p.top;
     select_topk<kSelNT>(key, n, k, p.top, out, sm);
     if (threadIdx.x == 0) p.block_count[((int64_t)b * p.Hq + h) * p.nb + a] = k;
 }
 
-// The same step with one wavefront per query block (rows of at most 64 R
-// blocks): the row lives in registers (block c = lane + 64 u in slot u), the
-// max and sum are butterfly reductions, and the selection is a 4-pass radix
-// select over 8-bit digits with a 256-bin LDS histogram per wavefront, then
-// one ordered ballot pass (slots in index order).  No workgroup barriers.
-constexpr int kWaveRows = 4;  // wavefronts (rows) per workgroup
-
+// Top-k of one row held by a wavefront: key[u] belongs to block
+// c = lane + 64 u (blocks c >= n absent, key 0).  Writes the count and the
+// ascending list padded with -1.  The k-th largest key T and how many keys
+// equal to T to take (the lowest blocks first) come from a bisection over
+// the key bits for rows of up to 512 blocks (the weights of a row share
+// their leading bits, which would put every key of a radix digit into one
+// bin), else from a 4-pass radix select over 8-bit digits with the
+// wavefront's 256-bin LDS histogram `hw`; then one ordered ballot pass
+// (slots in index order) writes the list.  No workgroup barriers.
 template <int R>
-__global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
-    __shared__ uint32_t hist[kWaveRows][256];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t rowid = (int64_t)blockIdx.x * kWaveRows + wv;
-    if (rowid >= (int64_t)p.B * p.n_heads * p.nb) return;
-    const int a = (int)(rowid % p.nb);
-    const int bl = (int)(rowid / p.nb);
-    const int b = bl / p.n_heads, li = bl % p.n_heads;
-    const int h = p.heads[li];
-    float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? h : li) * p.w_h + (int64_t)a * p.nb;
-    const int n = a + 1;
-    float x[R];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int c = lane + 64 * u;
-        x[u] = c < n ? W[c] : -INFINITY;
-        mx = fmaxf(mx, x[u]);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int c = lane + 64 * u;
-        x[u] = c < n ? fast_exp2((x[u] - mx) * kLog2e) : 0.f;
-        sum += x[u];
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    uint32_t key[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int c = lane + 64 * u;
-        const float wv = c < n ? x[u] / sum : 0.f;
-        if (c < p.nb) W[c] = wv;
-        key[u] = c >= n ? 0u : ((c == 0 || c == a) ? kForcedKey : order_key(wv));
-    }
-    const int k = min(p.top, n);
-    int32_t* out = p.block_idx + (((int64_t)b * p.Hq + h) * p.nb + a) * p.top;
-    if (lane == 0) p.block_count[((int64_t)b * p.Hq + h) * p.nb + a] = k;
-    for (int m = k + lane; m < p.top; m += 64) out[m] = -1;
+__device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int n, int top, int32_t* out,
+                                            int32_t* count, uint32_t* hw, int lane) {
+    const int k = min(top, n);
+    if (lane == 0) *count = k;
+    for (int m = k + lane; m < top; m += 64) out[m] = -1;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (k == n) {
         // every causal block is kept
@@ -237,8 +254,25 @@ __global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
         }
         return;
     }
-    // radix select: the k-th largest key T and how many keys == T to take
-    uint32_t* hw = hist[wv];
+    uint32_t T;
+    int need;
+    if constexpr (R <= 8) {
+        // short rows: the k-th largest key by bisection, one key bit per step
+        // (a compare and a ballot per slot), no LDS
+        T = 0u;
+#pragma unroll 1
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int ge = 0;
+#pragma unroll
+            for (int u = 0; u < R; ++u) ge += __popcll(__ballot(key[u] >= cand));  // absent keys are 0
+            if (ge >= k) T = cand;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int u = 0; u < R; ++u) gt += __popcll(__ballot(key[u] > T));
+        need = k - gt;
+    } else {
     uint32_t prefix = 0, pmask = 0;
     int rem = k;
 #pragma unroll 1
@@ -284,8 +318,9 @@ __global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
         pmask |= 255u << shift;
         __builtin_amdgcn_wave_barrier();
     }
-    const uint32_t T = prefix;
-    const int need = rem;
+    T = prefix;
+    need = rem;
+    }
     // ordered output: keys > T, then keys == T while fewer than `need` taken
     int run_eq = 0, run_sel = 0;
 #pragma unroll
@@ -302,6 +337,203 @@ __global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
     }
 }
 
+// Softmax of a row held by a wavefront, in place (slot u of block
+// c = lane + 64 u, blocks c >= n get 0); with WEIGHTS also stored to W[c]
+// for every c < nb.
+template <int R, bool WEIGHTS>
+__device__ __forceinline__ void wave_weights(float (&x)[R], int n, int nb, float* W, int lane) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < R; ++u) mx = fmaxf(mx, lane + 64 * u < n ? x[u] : -INFINITY);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        x[u] = lane + 64 * u < n ? fast_exp2((x[u] - mx) * kLog2e) : 0.f;
+        sum += x[u];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        x[u] = c < n ? x[u] / sum : 0.f;
+        if constexpr (WEIGHTS) {
+            if (c < nb) W[c] = x[u];
+        }
+    }
+}
+
+// The selection with one wavefront per query block (rows of at most 64 R
+// blocks), the row in registers (block c = lane + 64 u in slot u).
+constexpr int kWaveRows = 4;  // wavefronts (rows) per workgroup
+
+template <int R, bool WEIGHTS>
+__global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
+    __shared__ uint32_t hist[kWaveRows][256];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t rowid = (int64_t)blockIdx.x * kWaveRows + wv;
+    if (rowid >= (int64_t)p.B * p.n_heads * p.nb) return;
+    const int a = (int)(rowid % p.nb);
+    const int bl = (int)(rowid / p.nb);
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li];
+    float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? h : li) * p.w_h + (int64_t)a * p.nb;
+    const int n = a + 1;
+    float x[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        x[u] = c < n ? W[c] : -INFINITY;
+    }
+    wave_weights<R, WEIGHTS>(x, n, p.nb, W, lane);
+    uint32_t key[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int c = lane + 64 * u;
+        key[u] = c < n ? block_key(x[u], c, a) : 0u;
+    }
+    const int64_t row = ((int64_t)b * p.Hq + h) * p.nb + a;
+    wave_select<R>(key, n, p.top, p.block_idx + row * p.top, p.block_count + row, hist[wv], lane);
+}
+
+// Fused scores and selection for rows of at most kFusedMaxNb blocks: one
+// workgroup of eight wavefronts per (batch, listed head, strip of kStrip
+// query blocks) forms the strip's scores z[a][c] = scale * Qbar_a . Kbar_c
+// for every causal column in LDS, then each wavefront takes two rows from
+// LDS: softmax, top-k by weight.  The scores never reach memory; the weights
+// are written only when the caller asks.
+//
+// The scores are fp32 matrix-core products (v_mfma_f32_16x16x4_f32, A = the
+// strip's 16 query rows x 4 dimensions, B = 4 dimensions x 16 key blocks),
+// 256 columns at a time: wavefront w owns the 16-column blocks 2w, 2w+1 and
+// skips those past the strip's last causal column.  Kbar is staged in LDS in
+// chunks of kKc dimensions (row pitch 36 floats: the B reads of 16 rows x 4
+// dimensions hit distinct banks), the next chunk loaded while the current
+// one is used.  Lane l holds A[l % 16][l / 16], B[l / 16][l % 16] and
+// D[4 (l / 16) + r][l % 16], r < 4.
+constexpr int kStrip = 16;
+constexpr int kFusedMaxNb = 512;
+constexpr int kKc = 32;
+constexpr int kFusedNT = 512;
+constexpr int kKsPitch = 36;
+
+template <int D, bool WEIGHTS>
+__global__ void __launch_bounds__(kFusedNT) bs_fused(BsP p) {
+    constexpr int ZS = kFusedMaxNb + 4;
+    constexpr int R = kFusedMaxNb / 64;
+    constexpr int NW = kFusedNT / 64;
+    constexpr int RPW = kStrip / NW;  // rows selected per wavefront
+    __shared__ float zs[kStrip][ZS];
+    __shared__ __attribute__((aligned(16))) float qt[D][kStrip];  // Qbar^T of the strip
+    __shared__ __attribute__((aligned(16))) float ks[256][kKsPitch];
+    // the selection's histograms reuse the Kbar staging buffer, dead by then
+    static_assert(sizeof(ks) >= NW * 256 * sizeof(uint32_t), "histograms fit in the staging buffer");
+    uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(&ks[0][0]);
+    const int nstrip = (p.nb + kStrip - 1) / kStrip;
+    const int bl = blockIdx.x / nstrip, strip = blockIdx.x % nstrip;
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li];
+    const float* Q = p.qbar + (int64_t)bl * p.nb * D;
+    const float* K = p.kbar + ((int64_t)b * p.n_kv + p.kvslot[h / p.group]) * p.nb * D;
+    const int a0 = strip * kStrip;
+    const int rows = min(kStrip, p.nb - a0);
+    const int t = threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    {
+        // the strip's rows: all loads issued first (rows past nb read row 0)
+        float qv[kStrip * D / kFusedNT];
+#pragma unroll
+        for (int u = 0; u < kStrip * D / kFusedNT; ++u) {
+            const int e = u * kFusedNT + t;
+            const int r = e / D, d = e % D;
+            qv[u] = Q[(int64_t)(r < rows ? a0 + r : 0) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < kStrip * D / kFusedNT; ++u) {
+            const int e = u * kFusedNT + t;
+            const int r = e / D, d = e % D;
+            qt[d][r] = r < rows ? qv[u] : 0.f;
+        }
+    }
+    const int ncol = a0 + rows;
+    // Kbar chunks: 256 rows x kKc floats, one row per 8 lanes (float4 along
+    // d); all loads of a chunk are in flight together, rows past nb read row
+    // 0 and are zeroed when stored
+    constexpr int kLd = 256 * kKc / 4 / kFusedNT;
+    const int nchunk = (ncol + 255) / 256 * (D / kKc);
+    auto load_chunk = [&](int ci, f32x4 (&x)[kLd]) {
+        const int c0 = (ci / (D / kKc)) * 256, k0 = (ci % (D / kKc)) * kKc;
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+            const int e = u * kFusedNT + t;
+            const int c = c0 + e / (kKc / 4);
+            x[u] = *reinterpret_cast<const f32x4*>(K + (int64_t)(c < p.nb ? c : 0) * D + k0 + 4 * (e % (kKc / 4)));
+        }
+    };
+    f32x4 xb[kLd];
+    load_chunk(0, xb);
+    f32x4 acc[2];
+    const int ri = lane & 15, kq = lane >> 4;
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int c0 = (ci / (D / kKc)) * 256, k0 = (ci % (D / kKc)) * kKc;
+        if (k0 == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+            const int e = u * kFusedNT + t;
+            const int r = e / (kKc / 4), q4 = e % (kKc / 4);
+            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&ks[r][4 * q4]) = c0 + r < p.nb ? xb[u] : z0;
+        }
+        __syncthreads();
+        if (ci + 1 < nchunk) load_chunk(ci + 1, xb);
+        // the wavefront's column blocks that hold causal columns (uniform)
+        const int cb0 = 2 * wv;
+        const int nblk = min(2, max(0, (ncol - c0 - 16 * cb0 + 15) / 16));
+        if (nblk > 0) {
+#pragma unroll
+            for (int ks4 = 0; ks4 < kKc / 4; ++ks4) {
+                const float av = qt[k0 + 4 * ks4 + kq][ri];
+                const float b0 = ks[16 * cb0 + ri][4 * ks4 + kq];
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b0, acc[0], 0, 0, 0);
+                if (nblk > 1) {
+                    const float b1 = ks[16 * (cb0 + 1) + ri][4 * ks4 + kq];
+                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, acc[1], 0, 0, 0);
+                }
+            }
+        }
+        if (k0 + kKc < D) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = c0 + 16 * (cb0 + q) + ri;
+                if (c < ZS) zs[4 * kq + r][c] = acc[q][r] * p.scale;
+            }
+    }
+    __syncthreads();
+    for (int rr = RPW * wv; rr < RPW * wv + RPW && rr < rows; ++rr) {
+        const int a = a0 + rr, n = a + 1;
+        float x[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = lane + 64 * u;
+            x[u] = c < n ? zs[rr][c] : -INFINITY;
+        }
+        wave_weights<R, WEIGHTS>(x, n, p.nb, p.w + b * p.w_b + (int64_t)h * p.w_h + (int64_t)a * p.nb, lane);
+        uint32_t key[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = lane + 64 * u;
+            key[u] = c < n ? block_key(x[u], c, a) : 0u;
+        }
+        const int64_t row = ((int64_t)b * p.Hq + h) * p.nb + a;
+        wave_select<R>(key, n, p.top, p.block_idx + row * p.top, p.block_count + row, hist[wv], lane);
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -311,7 +543,8 @@ size_t bs_workspace_bytes(int32_t B, int32_t n_heads, int32_t Hkv, int32_t N, in
     const size_t nb = N / 64;
     size_t bytes = align256((size_t)B * n_heads * nb * D * sizeof(float));
     bytes += align256((size_t)B * Hkv * nb * D * sizeof(float));
-    if (!caller_scores) bytes += align256((size_t)B * n_heads * nb * nb * sizeof(float));
+    // scores between the two kernels of rows longer than the fused kernel takes
+    if (!caller_scores && nb > (size_t)kFusedMaxNb) bytes += align256((size_t)B * n_heads * nb * nb * sizeof(float));
     return bytes;
 }
 
@@ -357,38 +590,56 @@ hipError_t launch_block_estimate(const BsArgs& a, hipStream_t s) {
     p.block_count = a.block_count;
 
     const int pool_rows = a.B * (a.n_heads + nkv);
-    if (a.dtype == MI_BF16)
-        hipLaunchKernelGGL(bs_pool<uint16_t>, dim3(pool_rows * p.nb), dim3(128), 0, s, p);
-    else
-        hipLaunchKernelGGL(bs_pool<float>, dim3(pool_rows * p.nb), dim3(128), 0, s, p);
+    const dim3 pgrid((unsigned)(pool_rows * p.nb)), pblock(kPoolNT);
+    if (a.dtype == MI_BF16) {
+        if (a.D == 64) hipLaunchKernelGGL((bs_pool<uint16_t, 64>), pgrid, pblock, 0, s, p);
+        else hipLaunchKernelGGL((bs_pool<uint16_t, 128>), pgrid, pblock, 0, s, p);
+    } else {
+        if (a.D == 64) hipLaunchKernelGGL((bs_pool<float, 64>), pgrid, pblock, 0, s, p);
+        else hipLaunchKernelGGL((bs_pool<float, 128>), pgrid, pblock, 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const bool weights = a.w != nullptr;
+    if (p.nb <= kFusedMaxNb) {
+        const dim3 grid((unsigned)(a.B * a.n_heads * ((p.nb + kStrip - 1) / kStrip))), block(kFusedNT);
+        if (a.D == 64) {
+            if (weights) hipLaunchKernelGGL((bs_fused<64, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((bs_fused<64, false>), grid, block, 0, s, p);
+        } else {
+            if (weights) hipLaunchKernelGGL((bs_fused<128, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((bs_fused<128, false>), grid, block, 0, s, p);
+        }
+        return hipGetLastError();
+    }
     const int T = (p.nb + 63) / 64;
     hipLaunchKernelGGL(bs_scores, dim3(a.B * a.n_heads * (T * (T + 1) / 2)), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t sel_rows = (int64_t)a.B * a.n_heads * p.nb;
     const dim3 wgrid((unsigned)((sel_rows + kWaveRows - 1) / kWaveRows)), wblock(64 * kWaveRows);
-    if (p.nb <= 128) {
-        hipLaunchKernelGGL(bs_select_wave<2>, wgrid, wblock, 0, s, p);
-    } else if (p.nb <= 512) {
-        hipLaunchKernelGGL(bs_select_wave<8>, wgrid, wblock, 0, s, p);
-    } else if (p.nb <= 1024) {
-        hipLaunchKernelGGL(bs_select_wave<16>, wgrid, wblock, 0, s, p);
+#define MI_SEL_WAVE(R)                                                                   \
+    if (weights) hipLaunchKernelGGL((bs_select_wave<R, true>), wgrid, wblock, 0, s, p); \
+    else hipLaunchKernelGGL((bs_select_wave<R, false>), wgrid, wblock, 0, s, p);
+    if (p.nb <= 1024) {
+        MI_SEL_WAVE(16)
     } else if (p.nb <= 2048) {
-        hipLaunchKernelGGL(bs_select_wave<32>, wgrid, wblock, 0, s, p);
+        MI_SEL_WAVE(32)
     } else if (p.nb <= 4096) {
-        hipLaunchKernelGGL(bs_select_wave<64>, wgrid, wblock, 0, s, p);
+        MI_SEL_WAVE(64)
     } else {
         // longer rows: one workgroup per row, the row staged in LDS
         const size_t dyn = (size_t)p.nb * sizeof(float);
+        const void* fn = weights ? reinterpret_cast<const void*>(bs_select<true>)
+                                 : reinterpret_cast<const void*>(bs_select<false>);
         if (dyn > 48 * 1024) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(bs_select),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(bs_select, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
+        if (weights) hipLaunchKernelGGL(bs_select<true>, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
+        else hipLaunchKernelGGL(bs_select<false>, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
     }
+#undef MI_SEL_WAVE
     return hipGetLastError();
 }
 

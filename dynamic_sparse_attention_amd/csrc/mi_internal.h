@@ -84,6 +84,8 @@ struct TopkRows {
     TopkList list[2];
     uint32_t* scratch;  // topk_scratch_bytes(2 * B * n_heads) of device memory
 };
+// The first-digit histograms of the rows (mi_topk.h) must already be in
+// `scratch`, built by the score kernels after the scratch was cleared.
 hipError_t launch_topk_rows(const TopkRows& t, hipStream_t s);
 size_t topk_scratch_bytes(int32_t rows);
 

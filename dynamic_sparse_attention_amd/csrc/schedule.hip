@@ -26,7 +26,8 @@
 //     #{chunks with estimate > e}
 //   + #{chunks with estimate == e in sequences before s}
 //   + #{chunks of s before c with estimate == e},
-// each term a binary search per sequence.  mi_attn_schedule() returns the
+// each term a closed-form count per sequence (the estimate is a step
+// function of the run).  mi_attn_schedule() returns the
 // same order built on the host by a plain stable sort.
 #include <algorithm>
 #include <vector>
@@ -50,13 +51,20 @@ struct SchedShape {
     int32_t B, Hq, Hkv, nb, nruns, all_dense, sink, local, block_cap;
 };
 
-// Key blocks an item of this class is expected to visit.
+// Bound on the key blocks of an item of a sparse class (the causal span
+// bounds every class).
+__host__ __device__ inline long class_cap(int cls, const SchedShape& k) {
+    if (cls == 1) return (long)((k.sink + 63) / 64 + (k.local + 126) / 64 + kRunBlocks);
+    if (cls == 2) return (long)kRunBlocks * k.block_cap;
+    return (long)k.nb;
+}
+
+// Key blocks an item of this class is expected to visit:
+// min(4 (run + 1), nb, class bound), non-decreasing in the run.
 __host__ __device__ inline long estimate(int cls, int run, const SchedShape& k) {
     const long full = (long)(run + 1) * kRunBlocks;
     const long span = full < k.nb ? full : (long)k.nb;
-    long cap = span;
-    if (cls == 1) cap = (long)((k.sink + 63) / 64 + (k.local + 126) / 64 + kRunBlocks);
-    if (cls == 2) cap = (long)kRunBlocks * k.block_cap;
+    const long cap = class_cap(cls, k);
     return span < cap ? span : cap;
 }
 
@@ -111,15 +119,20 @@ struct SchedParams {
     uint8_t pattern[MI_MAX_HEADS];
 };
 
-// Sequence (g, class) of one batch entry: its heads and chunk count.
+// Sequence q = 3 g + class of one batch entry: its head count and chunks.
 struct Seq {
     int nh, nchunks;
 };
 
-__device__ inline Seq seq_of(const SchedParams& p, int g, int cls, int group) {
-    int nh = 0;
-    for (int h = g * group; h < (g + 1) * group; ++h)
-        nh += pattern_class(p.k.all_dense ? MI_DENSE : p.pattern[h]) == cls;
+// Head classes and per-sequence head counts, staged in LDS by each
+// workgroup once: the lookups below then never touch the argument memory.
+struct SchedLds {
+    uint8_t cls[MI_MAX_HEADS];
+    int16_t nh[3 * MI_MAX_HEADS];
+};
+
+__device__ inline Seq seq_of(const SchedParams& p, const SchedLds& L, int q) {
+    const int nh = L.nh[q];
     return Seq{nh, (p.k.nruns * nh + kChunk - 1) / kChunk};
 }
 
@@ -129,30 +142,39 @@ __device__ inline long chunk_est(const SchedParams& p, int cls, int nh, int c) {
     return estimate(cls, run, p.k);
 }
 
-// First chunk of the sequence whose estimate is <= e (strict = false: < e).
-__device__ inline int first_below(const SchedParams& p, int cls, const Seq& s, long e, bool strict) {
-    int lo = 0, hi = s.nchunks;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const long v = chunk_est(p, cls, s.nh, mid);
-        if (strict ? v < e : v <= e) hi = mid;
-        else lo = mid + 1;
-    }
-    return lo;
+// Number of chunks of a sequence whose estimate exceeds e.  The estimate
+// exceeds e exactly for runs >= R = floor(e / 4) (when nb and the class
+// bound exceed e at all), i.e. for item positions below nruns - R: the
+// first ceil((nruns - R) nh / 4) chunks.
+__device__ inline int count_above(const SchedParams& p, int cls, const Seq& s, long e) {
+    if ((long)p.k.nb <= e || class_cap(cls, p.k) <= e) return 0;
+    const long R = e / kRunBlocks < p.k.nruns ? e / kRunBlocks : (long)p.k.nruns;
+    const long n = ((p.k.nruns - R) * s.nh + kChunk - 1) / kChunk;
+    return (int)(n < s.nchunks ? n : s.nchunks);
 }
 
 __global__ void __launch_bounds__(kSchedThreads) attn_schedule_kernel(SchedParams p) {
+    __shared__ SchedLds L;
+    const int group = p.k.Hq / p.k.Hkv;
+    for (int h = threadIdx.x; h < p.k.Hq; h += kSchedThreads)
+        L.cls[h] = (uint8_t)pattern_class(p.k.all_dense ? MI_DENSE : p.pattern[h]);
+    __syncthreads();
+    for (int q = threadIdx.x; q < 3 * p.k.Hkv; q += kSchedThreads) {
+        int nh = 0;
+        for (int h = (q / 3) * group; h < (q / 3 + 1) * group; ++h) nh += L.cls[h] == q % 3;
+        L.nh[q] = (int16_t)nh;
+    }
+    __syncthreads();
     const int64_t t = (int64_t)blockIdx.x * kSchedThreads + threadIdx.x;
     const int64_t total = (int64_t)p.k.B * p.per_batch;
     if (t >= total) return;
-    const int group = p.k.Hq / p.k.Hkv;
     const int b = (int)(t / p.per_batch);
     int r = (int)(t % p.per_batch);
     // locate the thread's sequence (g, cls) and chunk c
     int g = 0, cls = 0;
     Seq s{0, 0};
     for (int q = 0; q < 3 * p.k.Hkv; ++q) {
-        s = seq_of(p, q / 3, q % 3, group);
+        s = seq_of(p, L, q);
         if (r < s.nchunks) {
             g = q / 3;
             cls = q % 3;
@@ -167,10 +189,10 @@ __global__ void __launch_bounds__(kSchedThreads) attn_schedule_kernel(SchedParam
     const int me = 3 * g + cls;
     for (int q = 0; q < 3 * p.k.Hkv; ++q) {
         const int cq = q % 3;
-        const Seq sq = seq_of(p, q / 3, cq, group);
+        const Seq sq = seq_of(p, L, q);
         if (sq.nchunks == 0) continue;
-        const int n_gt = first_below(p, cq, sq, e, false);  // chunks with estimate > e
-        const int n_ge = first_below(p, cq, sq, e, true);   // chunks with estimate >= e
+        const int n_gt = count_above(p, cq, sq, e);      // chunks with estimate > e
+        const int n_ge = count_above(p, cq, sq, e - 1);  // chunks with estimate >= e (e >= 1)
         gt += n_gt;
         eq_before += (int64_t)(n_ge - n_gt) * b + (q < me ? n_ge - n_gt : 0);
         if (q == me) eq_before += c - n_gt;
@@ -188,7 +210,7 @@ __global__ void __launch_bounds__(kSchedThreads) attn_schedule_kernel(SchedParam
             // the hk-th head of class cls in group g
             int h = g * group, seen = -1;
             for (; h < (g + 1) * group; ++h) {
-                seen += pattern_class(p.k.all_dense ? MI_DENSE : p.pattern[h]) == cls;
+                seen += L.cls[h] == cls;
                 if (seen == hk) break;
             }
             const int run = p.k.nruns - 1 - pos;

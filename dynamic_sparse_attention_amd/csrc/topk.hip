@@ -3,38 +3,41 @@
 // the sink and the main diagonal).  Exact and deterministic: selection by
 // (key desc, index asc) with order_key(), output ascending.
 //
-// A row is split into S segments, one 256-thread workgroup each, so that the
-// 2 rows per listed head keep the whole GPU busy.  Six launches over
-// (row, segment):
-//   0. clear the per-row global histograms;
-//   1-3. radix passes over 11/11/10-bit digits: every workgroup adds the
-//      histogram of its segment (restricted to the prefix found so far) to
-//      the row's global histogram with one atomic per non-empty bin, after
-//      finding the digit of the previous pass from that pass's complete
-//      histogram (every workgroup finds the same digit; segment 0 records it);
-//   4. with the k-th key T known, each wavefront counts the keys > T and == T
-//      of its contiguous slice of the segment;
-//   5. each wavefront writes the selected indices of its slice at the offset
-//      given by the counts of the slices before it: all keys > T, and keys
-//      == T while the row's first `need` of them (in index order) are not
-//      exhausted.
+// The key is resolved as three radix digits (mi_topk.h).  The histogram of
+// the first digit is built by the score kernels while they hold the scores,
+// so the rows are read here three times, in three launches over (row,
+// segment), a row being split into up to 64 segments of one 256-thread
+// workgroup so that the 2 rows per listed head keep the GPU busy:
+//   pass 2: finds digit 1 from its complete histogram (every workgroup finds
+//           the same digit; segment 0 records it) and adds the histogram of
+//           digit 2 over the keys with that prefix, one atomic per non-empty
+//           bin;
+//   pass 3: finds digit 2 the same way, so the 22-bit prefix P of the k-th
+//           key is known; each wavefront sweeps its contiguous slice of the
+//           segment, counts the keys above P and the keys sharing it, keeps
+//           the last digit of the first four of those, and adds them to the
+//           digit-3 histogram;
+//   write:  finds digit 3, hence the k-th key T and how many keys equal to T
+//           to take; each wavefront turns the slice records of the slices
+//           before it into its output offset (a slice holding more than four
+//           keys with prefix P is counted again by a sweep, which only
+//           degenerate rows with many near-equal scores need) and writes the
+//           selected indices of its slice: all keys > T, and keys == T while
+//           the row's first `need` of them (in index order) are not
+//           exhausted.
 // Histogram sums are integer atomics, whose totals do not depend on order.
 #include "mi_internal.h"
-#include "mi_select.h"
+#include "mi_topk.h"
 
 namespace mi {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kNW = kNT / 64;
-constexpr int kMaxSeg = 64;  // segments per row
-
-// Per-row scratch (uint32 words): three histograms, the state after each
-// pass (prefix, remaining rank) and the (gt, eq) counts of every wavefront
-// slice of every segment.
-constexpr int kHistWords = 2048 + 2048 + 1024;
-constexpr int kRowWords = kHistWords + 8 + 2 * kMaxSeg * kNW;
-constexpr int kBatch = 16;  // keys per lane loaded together by the count and write sweeps
+constexpr int kNW = kTopkNW;
+static_assert(kNT / 64 == kNW, "one slice per wavefront");
+constexpr int kBatch = 16;  // keys per lane loaded together by the slice sweeps
+constexpr uint32_t kMask1 = 0xFFC00000u;  // digit 1
+constexpr uint32_t kMask12 = 0xFFFFF800u;  // digits 1 and 2
 
 struct TopkP {
     TopkRows t;
@@ -61,19 +64,18 @@ __device__ __forceinline__ RowView row_view(const TopkP& p, int row) {
     v.budget = L.budget;
     v.forced = L.forced;
     v.n = t.n;
-    v.scr = t.scratch + (int64_t)row * kRowWords;
+    v.scr = t.scratch + (int64_t)row * kTopkRowWords;
     return v;
 }
 
-__device__ __forceinline__ uint32_t key_of(const RowView& v, int i) {
-    return i < v.forced ? kForcedKey : order_key(v.score[i]);
-}
+__device__ __forceinline__ uint32_t key_of(const RowView& v, int i) { return topk_key(v.score[i], i, v.forced); }
 
 struct Smem {
     uint32_t hist[2048];
     int32_t tot[kNW];
     uint32_t digit;
     int32_t above;
+    uint16_t list[kNW][kTopkSliceList];
 };
 
 // Finds, in a complete histogram of nbins bins, the bin that holds the
@@ -108,82 +110,6 @@ __device__ void find_bin(const uint32_t* hist, int nbins, int rem, Smem& sm, uin
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kNT) topk_clear(TopkP p) {
-    const int64_t words = (int64_t)2 * p.t.B * p.t.n_heads * kRowWords;
-    for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < words; i += (int64_t)gridDim.x * kNT)
-        p.t.scratch[i] = 0u;
-}
-
-// Radix pass `pass` (0..2) over segment s of a row.
-__global__ void __launch_bounds__(kNT) topk_hist(TopkP p, int pass) {
-    __shared__ Smem sm;
-    const int row = blockIdx.x / p.nseg, s = blockIdx.x % p.nseg;
-    const RowView v = row_view(p, row);
-    if (v.k >= v.n) return;  // everything is selected
-    uint32_t* st = v.scr + kHistWords;  // state: [pass] = (prefix, rem)
-    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
-    // the first keys are in flight while the previous digit is found
-    uint32_t kk[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int i = i0 + (int)threadIdx.x + u * kNT;
-        kk[u] = i < i1 ? key_of(v, i) : 0u;
-    }
-    uint32_t prefix = 0, pmask = 0;
-    int rem = v.k;
-    if (pass > 0) {
-        // the digit of the previous pass, from its complete histogram
-        const uint32_t* ph = v.scr + (pass == 1 ? 0 : 2048);
-        if (pass == 2) {
-            prefix = st[0];
-            rem = (int)st[1];
-        }
-        uint32_t d;
-        int above;
-        find_bin(ph, 2048, rem, sm, d, above);
-        const int shift = pass == 1 ? 21 : 10;
-        prefix |= d << shift;
-        rem -= above;
-        pmask = pass == 1 ? 0xFFE00000u : 0xFFFFFC00u;
-        if (s == 0 && threadIdx.x == 0) {
-            st[2 * (pass - 1)] = prefix;
-            st[2 * (pass - 1) + 1] = (uint32_t)rem;
-        }
-    }
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    for (int i = threadIdx.x; i < nbins; i += kNT) sm.hist[i] = 0u;
-    __syncthreads();
-    for (int base = i0 + (int)threadIdx.x; base < i1; base += 8 * kNT) {
-        if (base != i0 + (int)threadIdx.x) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = base + u * kNT;
-                kk[u] = i < i1 ? key_of(v, i) : 0u;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (base + u * kNT < i1 && (kk[u] & pmask) == prefix)
-                atomicAdd(&sm.hist[(kk[u] >> shift) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    uint32_t* gh = v.scr + (pass == 0 ? 0 : (pass == 1 ? 2048 : 4096));
-    for (int i = threadIdx.x; i < nbins; i += kNT)
-        if (sm.hist[i]) atomicAdd(&gh[i], sm.hist[i]);
-}
-
-// The threshold key T and the number of keys == T to take, from the last
-// histogram; every workgroup of the row finds the same values.
-__device__ void threshold(const RowView& v, Smem& sm, uint32_t& T, int& need) {
-    const uint32_t* st = v.scr + kHistWords;
-    uint32_t d;
-    int above;
-    find_bin(v.scr + 4096, 1024, (int)st[3], sm, d, above);
-    T = st[2] | d;
-    need = (int)st[3] - above;
-}
-
 // Keys of wavefront slice [w0, w1) in batches of kBatch per lane: lane l of
 // batch b holds key w0 + 64 (kBatch b + u) + l in kk[u] (0 past w1).
 __device__ __forceinline__ void load_batch(const RowView& v, int base, int w1, uint32_t (&kk)[kBatch]) {
@@ -195,43 +121,120 @@ __device__ __forceinline__ void load_batch(const RowView& v, int base, int w1, u
     }
 }
 
-// Each wavefront counts, over its contiguous slice of the segment (the
-// slices topk_write walks), the keys > T and == T.
-__global__ void __launch_bounds__(kNT) topk_count(TopkP p) {
+// Slice [w0, w1) of wavefront `wave` of segment s.
+__device__ __forceinline__ void slice_of(const TopkP& p, const RowView& v, int s, int wave, int& w0, int& w1) {
+    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
+    const int wseg = p.seg / kNW;
+    w0 = i0 + wave * wseg;
+    w1 = min(i1, w0 + wseg);
+}
+
+// Pass 2 over segment s of a row.
+__global__ void __launch_bounds__(kNT) topk_pass2(TopkP p) {
+    __shared__ Smem sm;
+    const int row = blockIdx.x / p.nseg, s = blockIdx.x % p.nseg;
+    const RowView v = row_view(p, row);
+    if (v.k >= v.n) return;  // everything is selected
+    uint32_t* st = v.scr + kTopkOffState;
+    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
+    // the first keys are in flight while digit 1 is found
+    uint32_t kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = i0 + (int)threadIdx.x + u * kNT;
+        kk[u] = i < i1 ? key_of(v, i) : 0u;
+    }
+    uint32_t d;
+    int above;
+    find_bin(v.scr, kTopkH1, v.k, sm, d, above);
+    const uint32_t prefix = d << 22;
+    if (s == 0 && threadIdx.x == 0) {
+        st[0] = prefix;
+        st[1] = (uint32_t)(v.k - above);
+    }
+    for (int i = threadIdx.x; i < kTopkH2; i += kNT) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int base = i0 + (int)threadIdx.x; base < i1; base += 8 * kNT) {
+        if (base != i0 + (int)threadIdx.x) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + u * kNT;
+                kk[u] = i < i1 ? key_of(v, i) : 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (base + u * kNT < i1 && (kk[u] & kMask1) == prefix) atomicAdd(&sm.hist[(kk[u] >> 11) & 2047u], 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = v.scr + kTopkOffH2;
+    for (int i = threadIdx.x; i < kTopkH2; i += kNT)
+        if (sm.hist[i]) atomicAdd(&gh[i], sm.hist[i]);
+}
+
+// Pass 3 over segment s of a row: digit-3 histogram and the slice records.
+__global__ void __launch_bounds__(kNT) topk_pass3(TopkP p) {
     __shared__ Smem sm;
     const int row = blockIdx.x / p.nseg, s = blockIdx.x % p.nseg;
     const RowView v = row_view(p, row);
     if (v.k >= v.n) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
-    const int wseg = p.seg / kNW;
-    const int w0 = i0 + wave * wseg, w1 = min(i1, w0 + wseg);
-    // the first batch of keys is in flight while the threshold is found
+    uint32_t* st = v.scr + kTopkOffState;
+    int w0, w1;
+    slice_of(p, v, s, wave, w0, w1);
     uint32_t kk[kBatch];
     load_batch(v, w0, w1, kk);
-    uint32_t T;
-    int need;
-    threshold(v, sm, T, need);
-    int gt = 0, eq = 0;
+    const int rem1 = (int)st[1];
+    uint32_t d;
+    int above;
+    find_bin(v.scr + kTopkOffH2, kTopkH2, rem1, sm, d, above);
+    const uint32_t P = st[0] | (d << 11);
+    if (s == 0 && threadIdx.x == 0) {
+        st[2] = P;
+        st[3] = (uint32_t)(rem1 - above);
+    }
+    for (int i = threadIdx.x; i < kTopkH3; i += kNT) sm.hist[i] = 0u;
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int gt = 0, eq = 0;  // eq: wave-uniform count of keys with prefix P so far
     for (int base = w0; base < w1; base += 64 * kBatch) {
         if (base != w0) load_batch(v, base, w1, kk);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const bool in = base + 64 * u + lane < w1;
-            gt += (in && kk[u] > T) ? 1 : 0;
-            eq += (in && kk[u] == T) ? 1 : 0;
+            const uint32_t hi = kk[u] & kMask12;
+            gt += (in && hi > P) ? 1 : 0;
+            const bool e = in && hi == P;
+            const uint64_t me = __ballot(e);
+            if (e) {
+                atomicAdd(&sm.hist[kk[u] & 2047u], 1u);
+                const int pos = eq + __popcll(me & below);
+                if (pos < kTopkSliceList) sm.list[wave][pos] = (uint16_t)(kk[u] & 2047u);
+            }
+            eq += __popcll(me);
         }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        gt += __shfl_xor(gt, off, 64);
-        eq += __shfl_xor(eq, off, 64);
-    }
+    for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off, 64);
+    __builtin_amdgcn_wave_barrier();
     if (lane == 0) {
-        uint32_t* wcnt = v.scr + kHistWords + 8 + 2 * (s * kNW + wave);
-        wcnt[0] = (uint32_t)gt;
-        wcnt[1] = (uint32_t)eq;
+        uint32_t* rec = v.scr + kTopkOffSlices + kTopkSliceWords * (s * kNW + wave);
+        uint32_t lo = 0u, hi2 = 0u;
+        const int nl = min(eq, kTopkSliceList);
+        for (int j = 0; j < nl; ++j) {
+            const uint32_t x = sm.list[wave][j];
+            if (j < 2) lo |= x << (16 * j);
+            else hi2 |= x << (16 * (j - 2));
+        }
+        rec[0] = (uint32_t)gt;
+        rec[1] = (uint32_t)eq;
+        rec[2] = lo;
+        rec[3] = hi2;
     }
+    __syncthreads();
+    uint32_t* gh = v.scr + kTopkOffH3;
+    for (int i = threadIdx.x; i < kTopkH3; i += kNT)
+        if (sm.hist[i]) atomicAdd(&gh[i], sm.hist[i]);
 }
 
 __global__ void __launch_bounds__(kNT) topk_write(TopkP p) {
@@ -245,23 +248,46 @@ __global__ void __launch_bounds__(kNT) topk_write(TopkP p) {
         return;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = s * p.seg, i1 = min(v.n, i0 + p.seg);
-    const int wseg = p.seg / kNW;
-    const int w0 = i0 + wave * wseg, w1 = min(i1, w0 + wseg);
+    int w0, w1;
+    slice_of(p, v, s, wave, w0, w1);
     // the first batch of keys is in flight while the threshold is found
     uint32_t kk[kBatch];
     load_batch(v, w0, w1, kk);
-    uint32_t T;
-    int need;
-    threshold(v, sm, T, need);
-    // selected entries and keys == T in the wavefront slices before this one
-    // (slices are ordered by key index: segment-major, then wavefront)
-    const uint32_t* wcnt = v.scr + kHistWords + 8;
+    const uint32_t* st = v.scr + kTopkOffState;
+    const int rem2 = (int)st[3];
+    uint32_t d3;
+    int above;
+    find_bin(v.scr + kTopkOffH3, kTopkH3, rem2, sm, d3, above);
+    const uint32_t T = st[2] | d3;
+    const int need = rem2 - above;
+    // selected entries and keys == T in the slices before this one (slices
+    // are ordered by key index: segment-major, then wavefront)
+    const uint32_t* recs = v.scr + kTopkOffSlices;
     const int before = s * kNW + wave;
     int sel_base = 0, eq_before = 0;
     for (int q = lane; q < before; q += 64) {
-        sel_base += (int)wcnt[2 * q];
-        eq_before += (int)wcnt[2 * q + 1];
+        const uint32_t* rec = recs + kTopkSliceWords * q;
+        const int eqn = (int)rec[1];
+        int g = 0, e = 0;
+        if (eqn <= kTopkSliceList) {
+            g = (int)rec[0];
+            for (int j = 0; j < eqn; ++j) {
+                const uint32_t x = (rec[2 + j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+                g += x > d3 ? 1 : 0;
+                e += x == d3 ? 1 : 0;
+            }
+        } else {
+            // many keys share the prefix: count the slice against T
+            int q0, q1;
+            slice_of(p, v, q / kNW, q % kNW, q0, q1);
+            for (int i = q0; i < q1; ++i) {
+                const uint32_t key = key_of(v, i);
+                g += key > T ? 1 : 0;
+                e += key == T ? 1 : 0;
+            }
+        }
+        sel_base += g;
+        eq_before += e;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -294,28 +320,23 @@ __global__ void __launch_bounds__(kNT) topk_write(TopkP p) {
 
 }  // namespace
 
-size_t topk_scratch_bytes(int32_t rows) { return (size_t)rows * kRowWords * sizeof(uint32_t); }
+size_t topk_scratch_bytes(int32_t rows) { return (size_t)rows * kTopkRowWords * sizeof(uint32_t); }
 
 hipError_t launch_topk_rows(const TopkRows& t, hipStream_t s) {
     TopkP p{t, 1, 0};
     const int rows = 2 * t.B * t.n_heads;
-    // segments of at least 4096 keys, at most kMaxSeg per row
+    // segments of at least 4096 keys, at most kTopkMaxSeg per row
     int nseg = (t.n + 4095) / 4096;
-    nseg = max(1, min(kMaxSeg, nseg));
+    nseg = max(1, min(kTopkMaxSeg, nseg));
     int seg = (t.n + nseg - 1) / nseg;
     seg = (seg + kNT - 1) / kNT * kNT;
     nseg = (t.n + seg - 1) / seg;
     p.nseg = nseg;
     p.seg = seg;
-    const int clear_blocks = min(1024, (int)((topk_scratch_bytes(rows) / 4 + kNT - 1) / kNT));
-    hipLaunchKernelGGL(topk_clear, dim3(clear_blocks), dim3(kNT), 0, s, p);
+    hipLaunchKernelGGL(topk_pass2, dim3(rows * nseg), dim3(kNT), 0, s, p);
     hipError_t e = hipGetLastError();
-    for (int pass = 0; pass < 3 && e == hipSuccess; ++pass) {
-        hipLaunchKernelGGL(topk_hist, dim3(rows * nseg), dim3(kNT), 0, s, p, pass);
-        e = hipGetLastError();
-    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_count, dim3(rows * nseg), dim3(kNT), 0, s, p);
+    hipLaunchKernelGGL(topk_pass3, dim3(rows * nseg), dim3(kNT), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_write, dim3(rows * nseg), dim3(kNT), 0, s, p);

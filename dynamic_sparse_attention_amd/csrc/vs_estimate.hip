@@ -24,6 +24,11 @@
 //   4. slash_combine adds those values of chunk c+1 into the top offsets of
 //      chunk c.
 // Every output is summed by one thread in a fixed order (deterministic).
+// The top-k that follows (topk.hip) takes its first radix histogram from
+// these kernels: rowstat_partial clears the top-k scratch, and each score
+// reaches the histogram of its row where it becomes final (in scores, or in
+// slash_combine for the offsets that receive a spill), so the top-k reads
+// the rows three times instead of five.
 //
 // Score layout (MFMA result, transposed): S^T (32 keys x 32 rows) = K . Q^T.
 // Lane l holds query row (l%32) of row block rb and keys
@@ -32,6 +37,7 @@
 
 #include "mi_device.h"
 #include "mi_internal.h"
+#include "mi_topk.h"
 
 namespace mi {
 namespace {
@@ -67,7 +73,16 @@ struct VsP {
     int64_t srow_b, srow_h;  // score row strides (elements)
     int32_t score_by_head;   // 1: row index is the head id, 0: the list position
     float* spill;            // [B*n_heads][nchunk2][kSpill] slash partials below each chunk's range
+    uint32_t* topk;          // top-k scratch, kTopkRowWords per score row (mi_topk.h)
+    int32_t topk_rows;       // 2 * B * n_heads
+    int32_t force_v, force_s;
 };
+
+// First-digit histograms of a head's two score rows: the keys are those the
+// top-k ranks (mi_topk.h), taken from the final score values.
+__device__ __forceinline__ uint32_t* topk_row(const VsP& p, int bl, int which) {
+    return p.topk + (int64_t)(2 * bl + which) * kTopkRowWords;
+}
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
     const float M = fmaxf(m, m2);
@@ -163,6 +178,11 @@ __global__ void __launch_bounds__(256) vs_rowstat_partial(VsP p) {
     __shared__ __attribute__((aligned(16))) char tiles[2][Kt::kBytes];
     const int nitems = p.B * p.nsets * p.nchunk1;
     const int L = blockIdx.x;
+    // the top-k histograms start at zero: cleared here, filled by the score
+    // kernels that follow on the stream
+    for (int64_t i = (int64_t)L * 256 + threadIdx.x; i < (int64_t)p.topk_rows * kTopkClearWords;
+         i += (int64_t)gridDim.x * 256)
+        p.topk[(i / kTopkClearWords) * kTopkRowWords + i % kTopkClearWords] = 0u;
     if (L >= nitems) return;
     const int chunk = L % p.nchunk1;
     const int bs = L / p.nchunk1;
@@ -297,6 +317,9 @@ __global__ void __launch_bounds__(256) vs_rowstat_combine(VsP p) {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) vs_scores(VsP p) {
     __shared__ float P[64 * kPitch2];
+    // first-digit histograms of the item's final scores: vertical counts in
+    // the low 16 bits, slash counts in the high 16 (at most 2048 each)
+    __shared__ uint32_t h1[kTopkH1];
     const int ngroups = (p.nchunk2 + kChunksPerItem - 1) / kChunksPerItem;
     const int nitems = p.B * p.n_heads * ngroups;
     const int L = chunked_xcd_remap(blockIdx.x, gridDim.x, p.group);
@@ -326,6 +349,7 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
     // [L-1-r, L-1-r+128)); the rest is cleared once and stays zero, so the
     // sums below run over all 64 rows without conditions.
     for (int i = t; i < 64 * kPitch2; i += 256) P[i] = 0.f;
+    for (int i = t; i < kTopkH1; i += 256) h1[i] = 0u;
     __syncthreads();
 
 #pragma unroll 1
@@ -373,7 +397,9 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
                 float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
                 for (int r = 0; r < 64; ++r) a[r & 3] += P[r * kPitch2 + t + Lq - 1 - r];
-                p.vscore[row_off + j] = (a[0] + a[1]) + (a[2] + a[3]);
+                const float vs = (a[0] + a[1]) + (a[2] + a[3]);
+                p.vscore[row_off + j] = vs;
+                atomicAdd(&h1[topk_digit1(topk_key(vs, j, p.force_v))], 1u);
             }
         } else {
             // slash partials: column x holds offset o = N - 1 - J0 - x
@@ -385,32 +411,59 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
                 const float a = (ap[0] + ap[1]) + (ap[2] + ap[3]);
                 const int o = p.N - 1 - J0 - x;
                 if (x < kChunk2) {
-                    if (o < p.N) p.sscore[row_off + o] = a;
+                    if (o < p.N) {
+                        p.sscore[row_off + o] = a;
+                        // final unless the chunk above spills into it
+                        if (x >= kSpill || chunk == p.nchunk2 - 1)
+                            atomicAdd(&h1[topk_digit1(topk_key(a, o, p.force_s))], 1u << 16);
+                    }
                 } else {
                     p.spill[((int64_t)bl * p.nchunk2 + chunk) * kSpill + (x - kChunk2)] = a;
                 }
             }
         }
     }
+    __syncthreads();
+    uint32_t* hv = topk_row(p, bl, 0);
+    uint32_t* hs = topk_row(p, bl, 1);
+    for (int i = t; i < kTopkH1; i += 256) {
+        const uint32_t c = h1[i];
+        if (c & 0xFFFFu) atomicAdd(&hv[i], c & 0xFFFFu);
+        if (c >> 16) atomicAdd(&hs[i], c >> 16);
+    }
 }
 
 // Adds the spill of chunk c+1 (offsets [128c+65, 128c+127]) into chunk c's
-// partial slash sums; one thread per (row, chunk, offset).
+// partial slash sums, which makes them final, and counts their first
+// digits.  One workgroup per (batch, listed head, kCombineChunks spilling
+// chunks), one thread per (chunk, offset).
+constexpr int kCombineChunks = 64;
+
 __global__ void __launch_bounds__(256) vs_slash_combine(VsP p) {
-    const int64_t total = (int64_t)p.B * p.n_heads * p.nchunk2 * kSpill;
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (g >= total) return;
-    const int k = (int)(g % kSpill);
-    const int64_t rc = g / kSpill;
-    const int chunk = (int)(rc % p.nchunk2);  // the spilling chunk c+1
-    const int bl = (int)(rc / p.nchunk2);
-    if (chunk == 0) return;  // offsets below 0 do not exist
+    __shared__ uint32_t h1[kTopkH1];
+    const int nseg = (p.nchunk2 + kCombineChunks - 1) / kCombineChunks;
+    const int bl = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int b = bl / p.n_heads, li = bl % p.n_heads;
     const int h = p.heads[li];
-    const int J0 = p.N - (chunk + 1) * kChunk2;
-    const int o = p.N - 1 - J0 - (kChunk2 + k);
     const int64_t row_off = b * p.srow_b + (int64_t)(p.score_by_head ? h : li) * p.srow_h;
-    p.sscore[row_off + o] += p.spill[g];
+    for (int i = threadIdx.x; i < kTopkH1; i += 256) h1[i] = 0u;
+    __syncthreads();
+    const int c0 = seg * kCombineChunks;
+    const int c1 = min(p.nchunk2, c0 + kCombineChunks);
+    for (int e = threadIdx.x; e < (c1 - c0) * kSpill; e += 256) {
+        const int chunk = c0 + e / kSpill;  // the spilling chunk c+1
+        const int k = e % kSpill;
+        if (chunk == 0) continue;  // offsets below 0 do not exist
+        const int J0 = p.N - (chunk + 1) * kChunk2;
+        const int o = p.N - 1 - J0 - (kChunk2 + k);
+        const float val = p.sscore[row_off + o] + p.spill[((int64_t)bl * p.nchunk2 + chunk) * kSpill + k];
+        p.sscore[row_off + o] = val;
+        atomicAdd(&h1[topk_digit1(topk_key(val, o, p.force_s))], 1u);
+    }
+    __syncthreads();
+    uint32_t* hs = topk_row(p, bl, 1);
+    for (int i = threadIdx.x; i < kTopkH1; i += 256)
+        if (h1[i]) atomicAdd(&hs[i], h1[i]);
 }
 
 template <typename T, int D>
@@ -426,8 +479,8 @@ hipError_t launch_t(VsP& p, hipStream_t s) {
     hipLaunchKernelGGL((vs_scores<T, D>), dim3(n2), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n3 = (int64_t)p.B * p.n_heads * p.nchunk2 * kSpill;
-    hipLaunchKernelGGL(vs_slash_combine, dim3((unsigned)((n3 + 255) / 256)), dim3(256), 0, s, p);
+    const int n3 = p.B * p.n_heads * ((p.nchunk2 + kCombineChunks - 1) / kCombineChunks);
+    hipLaunchKernelGGL(vs_slash_combine, dim3(n3), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -489,6 +542,10 @@ hipError_t launch_vs_estimate(const VsArgs& a, hipStream_t s) {
     off += align256((size_t)a.B * a.n_heads * p.nchunk2 * kSpill * sizeof(float));
     uint32_t* topk_scratch = reinterpret_cast<uint32_t*>(ws + off);
     off += align256(topk_scratch_bytes(2 * a.B * a.n_heads));
+    p.topk = topk_scratch;
+    p.topk_rows = 2 * a.B * a.n_heads;
+    p.force_v = a.force_vertical;
+    p.force_s = a.force_slash;
     if (a.vscore != nullptr) {
         // caller rows [B, Hq, N], indexed by head id
         p.vscore = a.vscore;

@@ -160,9 +160,13 @@ mi_status mi_vs_estimate(const mi_attn_desc* desc, const void* q, const void* k,
  *   heads        HOST int32[n_heads], strictly increasing q-head ids
  *   block_idx    int32 [batch, heads_q, nb, top_blocks]
  *   block_count  int32 [batch, heads_q, nb]
- *   block_score  float [batch, heads_q, nb, nb] (w) or NULL (then kept in ws)
+ *   block_score  float [batch, heads_q, nb, nb] (w) or NULL: w is then formed
+ *                only where the selection needs it and never stored; with
+ *                nb <= 512 the scores z stay on chip as well (one fused
+ *                kernel); longer rows keep z in ws between two kernels
  *   ws           >= mi_workspace_bytes(desc, MI_OP_BLOCK_ESTIMATE, n_heads, 0)
- * Requires top_blocks >= 2.  Equal weights rank the lower block first. */
+ * Requires top_blocks >= 2.  Equal weights rank the lower block first; the
+ * lists do not depend on whether block_score is given. */
 mi_status mi_block_estimate(const mi_attn_desc* desc, const void* q, const void* k,
                             const int32_t* heads, int32_t n_heads, int32_t top_blocks,
                             int32_t* block_idx, int32_t* block_count, float* block_score,

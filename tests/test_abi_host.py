@@ -90,7 +90,12 @@ def test_workspace_sizes():
     assert vs >= 2 * 2 * 1024 * 4 + 2 * 64 * 8
     bs = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_BLOCK_ESTIMATE, 2, 0)
     nb = 1024 // 64
-    assert bs >= (2 * nb * 128 + 2 * nb * 128 + 2 * nb * nb) * 4
+    # pooled query and key rows; rows of <= 512 blocks keep their scores on chip
+    assert bs >= (2 * nb * 128 + 2 * nb * 128) * 4
+    long = desc(seq_len=64 * 600, q_stride=(4 * 38400 * 128, 38400 * 128, 128),
+                k_stride=(38400 * 128, 38400 * 128, 128))
+    bs_long = l.mi_workspace_bytes(ctypes.byref(long), mi.OP_BLOCK_ESTIMATE, 2, 0)
+    assert bs_long >= (2 * 600 * 128 + 2 * 600 * 128 + 2 * 600 * 600) * 4
     # attention item schedule: one int32 per (batch, head, run of 4 query blocks) plus padding
     pf = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_SPARSE_PREFILL, 0, 0)
     assert pf >= 4 * 4 * (nb // 4) and pf % 256 == 0

@@ -226,16 +226,23 @@ def test_block_estimate(dtype, d, n, top):
 
 @pytest.mark.parametrize("nb", [128, 129, 512, 513, 700, 1024, 1025, 1500, 2048, 2049, 4096, 4097, 4200])
 def test_block_estimate_long_rows(nb):
-    """Every row of layers whose block count sits on each side of the select
-    kernel's dispatch boundaries: one wavefront per row holding 2, 8, 16, 32
-    or 64 register slots per lane (rows of up to 128, 512, 1024, 2048, 4096
-    blocks), and a workgroup per row above 4096 blocks."""
+    """Every row of layers whose block count sits on each side of the
+    estimate's dispatch boundaries: the fused scores+select kernel (rows of up
+    to 512 blocks), one wavefront per row holding 16, 32 or 64 register slots
+    per lane (rows of up to 1024, 2048, 4096 blocks), and a workgroup per row
+    above 4096 blocks; with and without the weights stored."""
     say(f"block_estimate long rows nb={nb}")
     n, d, top = 64 * nb, 64, 20
     _, (q, k, _), (q64, k64, _) = _inputs(14, 1, 1, n, d, "bf16")
     bidx, bcnt, w = mi.block_estimate(q, k, [0], top)
     torch.cuda.synchronize()
     bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    # without block_score: the weights are never stored (rows of up to 512
+    # blocks keep the scores on chip too), and the lists are identical
+    nb_idx, nb_cnt, none = mi.block_estimate(q, k, [0], top, return_scores=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert np.array_equal(nb_idx.cpu().numpy(), bidx) and np.array_equal(nb_cnt.cpu().numpy(), bcnt)
     rw, _ = O.bs_estimate(q64[0, 0], k64[0, 0], d ** -0.5, top)
     tri = np.tril(np.ones((nb, nb), bool))
     assert_scores_close(w[0, 0][tri], rw[tri], "block weights")
