@@ -483,6 +483,31 @@ __device__ __forceinline__ void s_compute(f32x16 (&s)[2], const char* kbuf, cons
     }
 }
 
+// S^T = K . Q^T with the K operands of the first two 16-dimension slices
+// already read (kpre[ks][kh]); bf16 only.
+template <typename T, int D>
+__device__ __forceinline__ void s_compute_pre(f32x16 (&s)[2], const char* kbuf, const LaneBase<T, D>& lb,
+                                              const QOperand<T, D>& qf,
+                                              const typename Elem<T>::frag (&kpre)[2][2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kh][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const typename Elem<T>::frag qk = qf.get(ks);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) mma32(s[kh], ks < 2 ? kpre[ks][kh] : k_frag<T, D>(kbuf, lb, kh, ks), qk);
+    }
+    constexpr int kReads = (D / 16 - 2) * 2;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8 - kReads, 0);
+}
+
 typedef __attribute__((address_space(4))) const uint32_t const_u32;
 __device__ __forceinline__ uint32_t ld_uniform_u32(const uint32_t* p) {
     return *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(p));
@@ -790,6 +815,16 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     // step t (K buffer kcur) and its mask.
     auto m_phase = [&](const char* kcur, const char* vprev, const int32_t* cpcur, bool pv_need, bool s_need,
                        f32x16 (&s)[2]) __attribute__((always_inline)) {
+        // bf16: the first S operands are read before the P.V chain (the K
+        // buffer is complete since the phase began), so that S starts
+        // without waiting on LDS
+        Frag kpre[2][2];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) kpre[ks][kh] = k_frag<T, D>(kcur, lb, kh, ks);
+        }
         if (pv_need) {
             if (rescale) {
 #pragma unroll
@@ -804,7 +839,8 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
             }
         }
         if (s_need) {
-            s_compute<T, D>(s, kcur, lb, qf);
+            if constexpr (sizeof(T) == 2) s_compute_pre<T, D>(s, kcur, lb, qf, kpre);
+            else s_compute<T, D>(s, kcur, lb, qf);
             mask_scores<EXACT>(s, step_mode<EXACT>(wcur, p, pattern, my_a), step_kb(wcur), cpcur, p, i_row, ex_bits,
                                my_a * 64 + (wave & 1) * 32);
         }
@@ -829,17 +865,17 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     // while group 0 issues the copy of V(t) and runs V(t).  K(t) sits in K
     // buffer t%2, V(t) in V buffer t%2; the loops unroll two steps so that
     // every buffer is a fixed LDS object in each copy.  Every wave waits for
-    // its own copies at the end of phase 2t+1.  Group 1's loop is rotated
-    // (M(t), barrier, copy of K(t+2), V(t)) so that a step's scores never
-    // cross an iteration.
+    // its own copies at the end of phase 2t+1.  A group-1 step is (copy of
+    // K(t+1), V(t-1), barrier, M(t)): the scores of step t-1 cross from one
+    // iteration into the next in s_keep.
     auto advance = [&](int t) __attribute__((always_inline)) {
         wprev = wcur;
         wcur = wnext;
         wnext = fetch(t + 2);
     };
-    // fp32 keeps its probabilities in the score registers until the next
-    // MFMA phase (s_keep: they cross the iteration there); bf16 scores are
-    // local to a step (sl).
+    // The scores of a step sit in s_keep from its MFMA phase to its vector
+    // phase (for group 1 across an iteration); fp32 then keeps its
+    // probabilities there up to the next MFMA phase, bf16 moves them to pfr.
     auto step0 = [&](int t, const char* kcur, char* vcur, const char* vprev, const int32_t* cpcur)
         __attribute__((always_inline)) {
         const bool pv_need = needs(wprev), s_need = needs(wcur);
