@@ -5,7 +5,8 @@
 # Usage: profile_layer.sh CONFIG OUTDIR   (CONFIG: c2, c3, c4, c5; run on a GPU
 # host from anywhere; writes OUTDIR/CONFIG/... and profiles/layer_kernels_*).
 # Each pass runs under its own time limit and the script stops at the first
-# failure.
+# failure.  With PROFILE_TABLES_ONLY=1 it only rebuilds the tables from the
+# CSV files already in OUTDIR (no GPU needed).
 set -u
 C=$1
 O=$(realpath -m "$2")
@@ -15,6 +16,9 @@ T=${PROFILE_PASS_SECONDS:-400}
 mkdir -p "$O/$C"
 cd /tmp && export TMPDIR=/tmp
 step() { echo "[profile_layer] $C: $1"; }
+if [ "${PROFILE_TABLES_ONLY:-0}" = 1 ]; then
+  :
+else
 if [ ! -d "$O/copy_fetch" ] || [ ! -d "$O/copy_write" ]; then
   step "copy calibration"
   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d "$O/copy_fetch" -o pmc --output-format csv -- python3 "$R/bench.py" --calibrate-copy > "$O/copy_fetch.log" 2>&1 || exit $?
@@ -28,6 +32,7 @@ step "WRITE_SIZE"
 timeout -s KILL "$T" rocprofv3 --pmc WRITE_SIZE -d "$O/$C/write" -o pmc --output-format csv -- python3 "$R/bench.py" --config "$C" $B --steps 1 --warmup 0 > "$O/$C.write.log" 2>&1 || exit $?
 step "SQ counters"
 timeout -s KILL "$T" rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVES -d "$O/$C/sq" -o pmc --output-format csv -- python3 "$R/bench.py" --config "$C" $B --steps 1 --warmup 0 > "$O/$C.sq.log" 2>&1 || exit $?
+fi
 step "tables"
 cd "$R" && python3 -m dynamic_sparse_attention_amd.profile_tables --workload "$C" --steps 3 \
   --trace "$O/$C/trace" --fetch "$O/$C/fetch" --write "$O/$C/write" --sq "$O/$C/sq" \

@@ -140,8 +140,10 @@ def algorithmic_bytes(w) -> dict:
         # the slash row (read and written)
         out["vs_slash_combine"] = hv * (N // 128) * (L - 1) * 12
         rows = 2 * hv
-        out["topk_hist"] = 3 * rows * N * 4  # three digit passes, one read each
-        out["topk_count"] = rows * N * 4
+        # the first digit's histogram comes from the score kernels; each of
+        # the three top-k launches reads the rows once
+        out["topk_pass2"] = rows * N * 4
+        out["topk_pass3"] = rows * N * 4
         out["topk_write"] = rows * N * 4 + hv * (nv + ns) * 4
         out["tile_set_kernel"] = hv * ns * 4 + hv * nb * 4
     if hb:
@@ -152,6 +154,9 @@ def algorithmic_bytes(w) -> dict:
         sel = hb * tri * 4 + hb * nb * (4 * min(w.top_blocks, nb) + 4)
         out["bs_select_wave"] = sel
         out["bs_select"] = sel
+        # fused scores + selection (rows of up to 512 blocks): the pooled rows
+        # in, the lists out
+        out["bs_fused"] = (hb + B * kv_bs) * nb * d * 4 + hb * nb * (4 * min(w.top_blocks, nb) + 4)
     out["build_index_kernel"] = B * Hq * nb * (4 * bcap + 4 * ccap + 8)
     out["sparse_attn_kernel"] = 2 * B * Hq * N * d * es + 2 * B * Hkv * N * d * es + B * Hq * N * 4
     return out
@@ -219,7 +224,7 @@ def build_record(args) -> dict:
             "kernels": rows}
 
 
-OWN_KERNELS = {"topk_clear", "attn_schedule_kernel", "vs_bits_kernel"}
+OWN_KERNELS = {"attn_schedule_kernel", "vs_bits_kernel"}
 
 
 def _fmt(v, nd=1):
