@@ -352,6 +352,11 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
     for (int i = t; i < kTopkH1; i += 256) h1[i] = 0u;
     __syncthreads();
 
+    // the K rows of a chunk are loaded while the previous chunk's
+    // probabilities and sums run (into the registers its MFMAs just read)
+    typename Elem<T>::frag kf[D / 16];
+    if (cg * kChunksPerItem < p.nchunk2)
+        unit_load<T, D>(p, kbase, p.N - (cg * kChunksPerItem + 1) * kChunk2 + wave * 32, rl, hl, kf);
 #pragma unroll 1
     for (int ci = 0; ci < kChunksPerItem; ++ci) {
         const int chunk = cg * kChunksPerItem + ci;
@@ -360,10 +365,10 @@ __global__ void __launch_bounds__(256) vs_scores(VsP p) {
         // chunk when N % 128 == 64 (those keys score zero)
         const int J0 = p.N - (chunk + 1) * kChunk2;
         const int key0 = J0 + wave * 32;
-        typename Elem<T>::frag kf[D / 16];
-        unit_load<T, D>(p, kbase, key0, rl, hl, kf);
         f32x16 acc[2];
         unit_mma<T, D>(p, key0, rl, kf, qf, acc);
+        if (ci + 1 < kChunksPerItem && chunk + 1 < p.nchunk2)
+            unit_load<T, D>(p, kbase, key0 - kChunk2, rl, hl, kf);
         if (ci > 0) __syncthreads();  // the previous chunk's sums have read the tile
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
