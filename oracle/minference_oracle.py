@@ -23,6 +23,9 @@ page (titles as printed on each page):
          (mean key of a 64-token block, query-block dot products, top-k key
          blocks, skipped tiles), section "1. The Vertical-Slash Kernel
          Mechanics" (online softmax with running max and normaliser).
+* [REVIEW] hysenlabs review of the MInference repository, section "How
+         MInference differs from xAttention, FlexPrefill and
+         RetrievalAttention": xAttention scores blocks by antidiagonal sums.
 
 Where the pages leave a step open the oracle takes one reading and the
 function says "reading:".  Every reading is listed with its justification in
@@ -259,6 +262,45 @@ def bs_estimate(q, k, scale, top_blocks, block=64):
     for a in range(nb):
         za = z[a, : a + 1]
         e = np.exp(za - za.max())
+        w[a, : a + 1] = e / e.sum()
+        kept.append(select_topk(w[a, : a + 1], min(top_blocks, a + 1), {0, a}))
+    return w, kept
+
+
+# ----------------------------------------------------------------------------
+# Antidiagonal block scoring ([REVIEW] "How MInference differs from
+# xAttention, FlexPrefill and RetrievalAttention": xAttention keeps the blocks
+# whose antidiagonal sums score highest)
+# ----------------------------------------------------------------------------
+
+def antidiag_estimate(q, k, scale, top_blocks, block=64):
+    """Block weights and kept key blocks of one head from antidiagonal sums.
+
+    Reading: the score of (query block a, key block c) is the sum of the
+    scaled logits along the block's main antidiagonal,
+        x[a, c] = scale * sum_r q[block*a + r] . k[block*c + block-1-r],
+    each query row and each key row of the pair entering once; for the
+    diagonal block c = a only its causal half (block-1-r <= r) is summed.
+    Then, as for the pooled estimate: w[a, :a+1] = softmax(x[a, :a+1]),
+    w[a, c] = 0 for c > a, and KB(a) = {0, a} plus the highest-weight other
+    causal blocks, min(top, a+1) in total.
+    Returns (w [nb, nb], list of ascending arrays KB(a)).
+    """
+    n, d = q.shape
+    nb = n // block
+    qb = q[: nb * block].reshape(nb, block, d)
+    kb = k[: nb * block].reshape(nb, block, d)[:, ::-1, :]  # row r of block c = key block*c + block-1-r
+    # x[a, c] = scale * sum_r qb[a, r] . kb[c, r]
+    x = scale * np.einsum("ard,crd->ac", qb, kb)
+    r = np.arange(block)
+    causal_half = (block - 1 - r) <= r
+    xdiag = scale * np.einsum("ard,ard->a", qb[:, causal_half], kb[:, causal_half])
+    w = np.zeros((nb, nb))
+    kept = []
+    for a in range(nb):
+        xa = x[a, : a + 1].copy()
+        xa[a] = xdiag[a]
+        e = np.exp(xa - xa.max())
         w[a, : a + 1] = e / e.sum()
         kept.append(select_topk(w[a, : a + 1], min(top_blocks, a + 1), {0, a}))
     return w, kept

@@ -398,3 +398,61 @@ def test_ashape_block_list_closed_form(s, w):
     for a in (0, 1, 2, 10, 64, 65, 79):
         ref = [c for c in range(a + 1) if 64 * c < s or 64 * (a - c) - 63 < w]
         assert list(O.ashape_block_list(a, s, w, n)) == ref
+
+
+# ----------------------------------------------------------------- antidiagonal block scoring
+
+def _antidiag_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "antidiag_b2_n6.txt")) if l.strip() and l[0] != "#"]
+    q = np.array([float(x) for x in rows[0][1:]])[:, None]
+    k = np.array([float(x) for x in rows[1][1:]])[:, None]
+    xs = {int(r[1]): [float(v) for v in r[3:]] for r in rows if r[0] == "x"}
+    kept = {(int(r[1].split("=")[1]), int(r[2])): [int(v) for v in r[4:]] for r in rows if r[0] == "kept"}
+    return q, k, xs, kept
+
+
+def test_antidiag_golden():
+    """Hand-worked scores: the oracle's weights are scipy's softmax of them and
+    its kept lists are the worked ones (block 1 outscores block 2 in row 2 and
+    is still dropped at top 2: blocks 0 and a are forced)."""
+    from scipy.special import softmax
+    q, k, xs, kept = _antidiag_golden()
+    for top in (2, 3):
+        w, kb = O.antidiag_estimate(q, k, 1.0, top, block=2)
+        for a, x in xs.items():
+            np.testing.assert_allclose(w[a, : a + 1], softmax(np.array(x)), rtol=1e-13)
+            assert not w[a, a + 1:].any()
+        for (t, a), lst in kept.items():
+            if t == top:
+                assert list(kb[a]) == lst, (top, a)
+
+
+def test_antidiag_block_size_one_is_causal_softmax():
+    """With one-token blocks the antidiagonal is the logit itself: the weights
+    are the causal attention probabilities (scipy softmax at an explicit
+    scale) and the lists the per-token top-k."""
+    from scipy.special import softmax
+    g = np.random.default_rng(41)
+    n, d, sc = 23, 5, 0.43
+    q, k = g.standard_normal((n, d)), g.standard_normal((n, d))
+    w, kept = O.antidiag_estimate(q, k, sc, 4, block=1)
+    for i in range(n):
+        np.testing.assert_allclose(w[i, : i + 1], softmax(sc * (k[: i + 1] @ q[i])), rtol=1e-12)
+        assert list(kept[i]) == list(O.select_topk(w[i, : i + 1], min(4, i + 1), {0, i}))
+
+
+def test_antidiag_constant_blocks_match_pooled_estimate():
+    """Rows constant inside each block: off the diagonal x = block * z of the
+    pooled estimate (a closed form), the diagonal block sums its causal half
+    (block/2 pairs); the kept lists equal the pooled estimate's."""
+    g = np.random.default_rng(43)
+    nb, b, d, sc = 9, 8, 6, 0.3
+    qm, km = g.standard_normal((nb, d)), g.standard_normal((nb, d))
+    q, k = np.repeat(qm, b, axis=0), np.repeat(km, b, axis=0)
+    w, kept = O.antidiag_estimate(q, k, sc, 4, block=b)
+    _, kept_pool = O.bs_estimate(q, k, sc, 4, block=b)
+    for a in range(nb):
+        x = np.array([b * sc * qm[a] @ km[c] for c in range(a)] + [(b // 2) * sc * qm[a] @ km[a]])
+        e = np.exp(x - x.max())
+        np.testing.assert_allclose(w[a, : a + 1], e / e.sum(), rtol=1e-12)
+        assert list(kept[a]) == list(kept_pool[a]), a
