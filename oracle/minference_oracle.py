@@ -290,11 +290,12 @@ def antidiag_estimate(q, k, scale, top_blocks, block=64):
     nb = n // block
     qb = q[: nb * block].reshape(nb, block, d)
     kb = k[: nb * block].reshape(nb, block, d)[:, ::-1, :]  # row r of block c = key block*c + block-1-r
-    # x[a, c] = scale * sum_r qb[a, r] . kb[c, r]
-    x = scale * np.einsum("ard,crd->ac", qb, kb)
+    # x[a, c] = scale * sum_r qb[a, r] . kb[c, r]: a matrix product over the
+    # block's rows laid end to end
+    x = scale * (qb.reshape(nb, block * d) @ kb.reshape(nb, block * d).T)
     r = np.arange(block)
     causal_half = (block - 1 - r) <= r
-    xdiag = scale * np.einsum("ard,ard->a", qb[:, causal_half], kb[:, causal_half])
+    xdiag = scale * (qb[:, causal_half] * kb[:, causal_half]).sum(axis=(1, 2))
     w = np.zeros((nb, nb))
     kept = []
     for a in range(nb):
