@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal comparator")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token secondary measurement")
     ap.add_argument("--no-gather", action="store_true", help="skip the isolated column-gather rate")
+    ap.add_argument("--no-antidiag", action="store_true", help="skip the antidiagonal block estimate")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact (element-masked) Vertical-Slash variant and the clustered-slash layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -345,6 +346,37 @@ def gather_rate(q, k, v, w, n_vertical=1000):
                     "from L2/MALL as much as from HBM"}
 
 
+def antidiag_rate(q, k, w):
+    """The antidiagonal block estimate (scores, softmax, top-k) of every head
+    of the layer, weights not stored: median of three launches.  FLOP are the
+    definition's: 2*64*d per (query block, earlier key block) pair and 2*32*d
+    per diagonal pair."""
+    import torch
+    import dynamic_sparse_attention_amd as mi
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    heads = list(range(Hq))
+    dev = q.device
+    outs = (torch.zeros((B, Hq, nb, w.top_blocks), dtype=torch.int32, device=dev),
+            torch.zeros((B, Hq, nb), dtype=torch.int32, device=dev), None)
+    mi.antidiag_estimate(q, k, heads, w.top_blocks, return_scores=False, outputs=outs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mi.antidiag_estimate(q, k, heads, w.top_blocks, return_scores=False, outputs=outs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    flop = B * Hq * (2.0 * 64 * d * nb * (nb - 1) / 2 + 2.0 * 32 * d * nb)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 3), "flop": flop, "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "scores as a dense contraction over 64*d per block pair (MFMA), then the block softmax and top-k"}
+
+
 def sampled_parity(plan, w, data, n_items=8):
     """Attention rows of the plan (relaunched on its index, since the dense
     comparator shares the output buffer) against the oracle fed the GPU's
@@ -474,6 +506,9 @@ def main():
     if not args.no_gather and w.seq_len >= 65536 and w.dtype == "bf16":
         log("[bench] column gather rate")
         out["gather"] = gather_rate(plan.q, plan.k, plan.v, w)
+    if not args.no_antidiag:
+        log("[bench] antidiagonal block estimate")
+        out["antidiag_estimate"] = antidiag_rate(plan.q, plan.k, w)
     if not args.no_exact and any(p == W.VSLASH for p in plan.pat):
         # the same layer with the Vertical-Slash heads element-masked to their
         # exact key sets: attention time on the same estimate and index lists

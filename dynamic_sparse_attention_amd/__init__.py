@@ -26,11 +26,11 @@ MI_MAX_HEADS = 256
 MI_F32, MI_BF16 = 0, 1
 ASHAPE, VSLASH, BSPARSE, DENSE, VSLASH_EXACT = 0, 1, 2, 3, 4
 VS_PATTERNS = (VSLASH, VSLASH_EXACT)
-OP_VS_ESTIMATE, OP_BLOCK_ESTIMATE, OP_SPARSE_PREFILL = 0, 1, 2
+OP_VS_ESTIMATE, OP_BLOCK_ESTIMATE, OP_SPARSE_PREFILL, OP_ANTIDIAG_ESTIMATE = 0, 1, 2, 3
 STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_BUDGET", 4: "MI_ERR_DTYPE",
           5: "MI_ERR_WORKSPACE", 6: "MI_ERR_LAUNCH", 7: "MI_ERR_PATTERN"}
 
-EXPORTS = ("mi_workspace_bytes", "mi_vs_estimate", "mi_block_estimate", "mi_build_index",
+EXPORTS = ("mi_workspace_bytes", "mi_vs_estimate", "mi_block_estimate", "mi_antidiag_estimate", "mi_build_index",
            "mi_sparse_prefill", "mi_sparse_prefill_noalloc", "mi_attn_schedule", "mi_status_str",
            "mi_last_error")
 NOALLOC_SCHEDULE_ENTRIES = 1 << 18
@@ -66,6 +66,8 @@ _SIGS = {
                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "mi_block_estimate": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _I, _I, _P, _P, _P, _P,
                                ctypes.c_size_t, _P]),
+    "mi_antidiag_estimate": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _I, _I, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
     "mi_build_index": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _I, _P, _I, _P, _P, _I, _I, _I,
                             ctypes.POINTER(MiIndex), _P]),
     "mi_sparse_prefill": (_I, [ctypes.POINTER(MiAttnDesc), _P, _P, _P, _P, ctypes.POINTER(MiIndex),
@@ -200,6 +202,30 @@ def block_estimate(q, k, heads: Sequence[int], top_blocks: int = 100, scale: Opt
     _check(lib().mi_block_estimate(ctypes.byref(desc), _ptr(q), _ptr(k), ctypes.cast(hs, _P), len(heads),
                                    top_blocks, _ptr(bidx), _ptr(bcnt), _ptr(w), _ptr(ws), ws.numel(),
                                    _stream(stream)))
+    return bidx, bcnt, w
+
+
+def antidiag_estimate(q, k, heads: Sequence[int], top_blocks: int = 100, scale: Optional[float] = None,
+                   return_scores: bool = True, outputs=None, stream=None):
+    """Block-Sparse lists from antidiagonal block scores (see
+    mi_antidiag_estimate).  Returns (block_idx [B,Hq,nb,top], block_count
+    [B,Hq,nb], block_score [B,Hq,nb,nb] | None)."""
+    desc = make_desc(q, k, scale=scale)
+    B, Hq, N, _ = q.shape
+    nb = N // MI_BLOCK
+    dev = q.device
+    if outputs is None:
+        bidx = torch.zeros((B, Hq, nb, top_blocks), dtype=torch.int32, device=dev)
+        bcnt = torch.zeros((B, Hq, nb), dtype=torch.int32, device=dev)
+        w = torch.zeros((B, Hq, nb, nb), dtype=torch.float32, device=dev) if return_scores else None
+    else:
+        bidx, bcnt, w = outputs
+    need = lib().mi_workspace_bytes(ctypes.byref(desc), OP_ANTIDIAG_ESTIMATE, len(heads), 0)
+    ws = _workspace(need, dev)
+    hs = _heads_arr(heads)
+    _check(lib().mi_antidiag_estimate(ctypes.byref(desc), _ptr(q), _ptr(k), ctypes.cast(hs, _P), len(heads),
+                                      top_blocks, _ptr(bidx), _ptr(bcnt), _ptr(w), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
     return bidx, bcnt, w
 
 

@@ -218,6 +218,7 @@ size_t mi_workspace_bytes(const mi_attn_desc* d, int32_t op, int32_t p0, int32_t
             return mi::bs_workspace_bytes(d->batch, p0, d->heads_kv, d->seq_len, d->head_dim, false);
         case MI_OP_SPARSE_PREFILL:
             return (mi::attn_schedule_bytes(d->batch, d->heads_q, d->heads_kv, d->seq_len) + 255) & ~size_t(255);
+        case MI_OP_ANTIDIAG_ESTIMATE: return mi::ad_workspace_bytes(d->batch, p0, d->seq_len, false);
     }
     return 0;
 }
@@ -268,6 +269,7 @@ mi_status mi_block_estimate(const mi_attn_desc* d, const void* q, const void* k,
     mi_status st = check_desc(d);
     if (st != MI_OK) return st;
     if (!q || !k || !block_idx || !block_count) return fail(MI_ERR_NULL, "q, k, block_idx or block_count is NULL");
+    if (!aligned16(q) || !aligned16(k)) return fail(MI_ERR_SHAPE, "q and k must be 16-byte aligned");
     if ((st = check_heads(d, heads, n_heads)) != MI_OK) return st;
     if (top_blocks < 2) return fail(MI_ERR_BUDGET, "top_blocks %d must be >= 2 (blocks 0 and a are kept)", top_blocks);
     const int nb = d->seq_len / MI_BLOCK;
@@ -290,6 +292,36 @@ mi_status mi_block_estimate(const mi_attn_desc* d, const void* q, const void* k,
     a.w = block_score;
     a.ws = ws;
     return launched(mi::launch_block_estimate(a, static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_antidiag_estimate(const mi_attn_desc* d, const void* q, const void* k, const int32_t* heads,
+                               int32_t n_heads, int32_t top_blocks, int32_t* block_idx, int32_t* block_count,
+                               float* block_score, void* ws, size_t ws_bytes, void* stream) {
+    mi_status st = check_desc(d);
+    if (st != MI_OK) return st;
+    if (!q || !k || !block_idx || !block_count) return fail(MI_ERR_NULL, "q, k, block_idx or block_count is NULL");
+    if (!aligned16(q) || !aligned16(k)) return fail(MI_ERR_SHAPE, "q and k must be 16-byte aligned");
+    if ((st = check_heads(d, heads, n_heads)) != MI_OK) return st;
+    if (top_blocks < 2) return fail(MI_ERR_BUDGET, "top_blocks %d must be >= 2 (blocks 0 and a are kept)", top_blocks);
+    const int nb = d->seq_len / MI_BLOCK;
+    if ((size_t)nb * 4 + 12 * 1024 > kMaxLds)
+        return fail(MI_ERR_SHAPE, "seq_len %d too long for the block estimate (nb <= %zu)", d->seq_len,
+                    (kMaxLds - 12 * 1024) / 4);
+    const size_t need = mi::ad_workspace_bytes(d->batch, n_heads, d->seq_len, block_score != nullptr);
+    if (ws_bytes < need || !ws) return fail(MI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    mi::BsArgs a{};
+    a.q = q; a.k = k;
+    copy_strides(a.qs, d->q_stride);
+    copy_strides(a.ks, d->k_stride);
+    a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.N = d->seq_len; a.D = d->head_dim;
+    a.dtype = d->dtype; a.scale = d->scale;
+    a.n_heads = n_heads;
+    for (int i = 0; i < n_heads; ++i) a.heads[i] = heads[i];
+    a.top = top_blocks;
+    a.block_idx = block_idx; a.block_count = block_count;
+    a.w = block_score;
+    a.ws = ws;
+    return launched(mi::launch_antidiag_estimate(a, static_cast<hipStream_t>(stream)));
 }
 
 mi_status mi_build_index(const mi_attn_desc* d, const int32_t* head_pattern, const int32_t* vertical_idx,

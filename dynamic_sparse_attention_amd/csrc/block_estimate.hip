@@ -534,7 +534,119 @@ __global__ void __launch_bounds__(kFusedNT) bs_fused(BsP p) {
     }
 }
 
+// Antidiagonal block scores (hysenlabs review, "How MInference differs from
+// xAttention, FlexPrefill and RetrievalAttention": blocks scored by
+// antidiagonal sums):
+//     x[a][c] = scale * sum_r q[64a + r] . k[64c + 63 - r],   c <= a,
+// over the causal half r >= 32 only for c = a.  As a matrix, X = Qt . Kt^T
+// with Qt[a] the 64 rows of query block a laid end to end and Kt[c] those of
+// key block c in reverse order: a dense contraction over 64 d, so on MFMA.
+// One wavefront per 32x32 tile of X (query blocks 32 ta + i, key blocks
+// 32 tc + j, tc <= ta): for each r it reads query row 64a + r and key row
+// 64c + 63 - r as operand fragments (transposed form, as the Vertical-Slash
+// estimate: lane l holds query block l % 32 and key blocks
+// 8 (e/4) + 4 (l/32) + e % 4 of acc[e]).  On a diagonal tile the lane whose
+// key block equals its query block keeps the sum after r = 31 and subtracts
+// it at the end.  The scores go to the score rows that the selection kernels
+// then turn into weights and lists.
+constexpr int kAdWaves = 4;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64 * kAdWaves) ad_scores(BsP p) {
+    typedef typename Elem<T>::frag Frag;
+    const int T32 = (p.nb + 31) / 32;
+    const int per = T32 * (T32 + 1) / 2;  // lower-triangle tiles per listed head
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * kAdWaves + wv;
+    if (item >= (int64_t)p.B * p.n_heads * per) return;
+    const int bl = (int)(item / per);
+    int x = (int)(item % per);
+    int ta = 0;
+    while (x >= ta + 1) {
+        x -= ta + 1;
+        ++ta;
+    }
+    const int tc = x;
+    const int b = bl / p.n_heads, li = bl % p.n_heads;
+    const int h = p.heads[li];
+    const int rl = lane & 31, hl = lane >> 5;
+    const int a = 32 * ta + rl;             // this lane's query block
+    const int ca = a < p.nb ? a : p.nb - 1;  // rows read for blocks past nb (not written)
+    const int cb = min(32 * tc + rl, p.nb - 1);
+    const T* qrow0 = reinterpret_cast<const T*>(p.q) + b * p.qs0 + h * p.qs1 + (int64_t)ca * 64 * p.qs2 + 8 * hl;
+    const T* krow0 = reinterpret_cast<const T*>(p.k) + b * p.ks0 + (h / p.group) * p.ks1 +
+                     ((int64_t)cb * 64 + 63) * p.ks2 + 8 * hl;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    // the diagonal entry of this lane (key block == query block), if any
+    const bool diag_tile = ta == tc;
+    const int e_d = ((rl >> 3) << 2) | (rl & 3);
+    const bool has_d = diag_tile && ((rl >> 2) & 1) == hl;
+    float d_low = 0.f;
+#pragma unroll 2
+    for (int r = 0; r < 64; ++r) {
+        Frag qf[D / 16], kf[D / 16];
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            qf[s] = load_frag(qrow0 + (int64_t)r * p.qs2 + 16 * s);
+            kf[s] = load_frag(krow0 - (int64_t)r * p.ks2 + 16 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) mma32(acc, kf[s], qf[s]);
+        if (r == 31 && has_d) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (e == e_d) d_low = acc[e];
+        }
+    }
+    if (a >= p.nb) return;
+    float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? h : li) * p.w_h + (int64_t)a * p.nb;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int c = 32 * tc + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (c > a || c >= p.nb) continue;
+        const float v = (c == a) ? acc[e] - d_low : acc[e];
+        W[c] = v * p.scale;
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Softmax and top-k of the score rows p.w (weights written back when asked).
+hipError_t launch_select(BsP& p, bool weights, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    const int64_t sel_rows = (int64_t)p.B * p.n_heads * p.nb;
+    const dim3 wgrid((unsigned)((sel_rows + kWaveRows - 1) / kWaveRows)), wblock(64 * kWaveRows);
+#define MI_SEL_WAVE(R)                                                                   \
+    if (weights) hipLaunchKernelGGL((bs_select_wave<R, true>), wgrid, wblock, 0, s, p); \
+    else hipLaunchKernelGGL((bs_select_wave<R, false>), wgrid, wblock, 0, s, p);
+    if (p.nb <= 128) {
+        MI_SEL_WAVE(2)
+    } else if (p.nb <= 512) {
+        MI_SEL_WAVE(8)
+    } else if (p.nb <= 1024) {
+        MI_SEL_WAVE(16)
+    } else if (p.nb <= 2048) {
+        MI_SEL_WAVE(32)
+    } else if (p.nb <= 4096) {
+        MI_SEL_WAVE(64)
+    } else {
+        // longer rows: one workgroup per row, the row staged in LDS
+        const size_t dyn = (size_t)p.nb * sizeof(float);
+        const void* fn = weights ? reinterpret_cast<const void*>(bs_select<true>)
+                                 : reinterpret_cast<const void*>(bs_select<false>);
+        if (dyn > 48 * 1024) {
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            if (e != hipSuccess) return e;
+        }
+        if (weights) hipLaunchKernelGGL(bs_select<true>, dim3(p.B * p.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
+        else hipLaunchKernelGGL(bs_select<false>, dim3(p.B * p.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
+    }
+#undef MI_SEL_WAVE
+    return hipGetLastError();
+}
+
 
 }  // namespace
 
@@ -616,31 +728,52 @@ hipError_t launch_block_estimate(const BsArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bs_scores, dim3(a.B * a.n_heads * (T * (T + 1) / 2)), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t sel_rows = (int64_t)a.B * a.n_heads * p.nb;
-    const dim3 wgrid((unsigned)((sel_rows + kWaveRows - 1) / kWaveRows)), wblock(64 * kWaveRows);
-#define MI_SEL_WAVE(R)                                                                   \
-    if (weights) hipLaunchKernelGGL((bs_select_wave<R, true>), wgrid, wblock, 0, s, p); \
-    else hipLaunchKernelGGL((bs_select_wave<R, false>), wgrid, wblock, 0, s, p);
-    if (p.nb <= 1024) {
-        MI_SEL_WAVE(16)
-    } else if (p.nb <= 2048) {
-        MI_SEL_WAVE(32)
-    } else if (p.nb <= 4096) {
-        MI_SEL_WAVE(64)
+    return launch_select(p, weights, s);
+}
+
+size_t ad_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_scores) {
+    const size_t nb = N / 64;
+    return caller_scores ? 256 : align256((size_t)B * n_heads * nb * nb * sizeof(float));
+}
+
+hipError_t launch_antidiag_estimate(const BsArgs& a, hipStream_t s) {
+    BsP p{};
+    p.q = static_cast<const char*>(a.q);
+    p.k = static_cast<const char*>(a.k);
+    p.qs0 = a.qs[0]; p.qs1 = a.qs[1]; p.qs2 = a.qs[2];
+    p.ks0 = a.ks[0]; p.ks1 = a.ks[1]; p.ks2 = a.ks[2];
+    p.B = a.B; p.Hq = a.Hq; p.N = a.N; p.nb = a.N / 64; p.D = a.D;
+    p.group = a.Hq / a.Hkv;
+    p.n_heads = a.n_heads; p.top = a.top; p.scale = a.scale;
+    for (int i = 0; i < a.n_heads; ++i) p.heads[i] = a.heads[i];
+    const int64_t nb2 = (int64_t)p.nb * p.nb;
+    const bool weights = a.w != nullptr;
+    if (weights) {
+        p.w = a.w;
+        p.w_b = (int64_t)a.Hq * nb2;
+        p.w_h = nb2;
+        p.w_by_head = 1;
     } else {
-        // longer rows: one workgroup per row, the row staged in LDS
-        const size_t dyn = (size_t)p.nb * sizeof(float);
-        const void* fn = weights ? reinterpret_cast<const void*>(bs_select<true>)
-                                 : reinterpret_cast<const void*>(bs_select<false>);
-        if (dyn > 48 * 1024) {
-            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-            if (e != hipSuccess) return e;
-        }
-        if (weights) hipLaunchKernelGGL(bs_select<true>, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
-        else hipLaunchKernelGGL(bs_select<false>, dim3(a.B * a.n_heads * p.nb), dim3(kSelNT), dyn, s, p);
+        p.w = static_cast<float*>(a.ws);
+        p.w_b = (int64_t)a.n_heads * nb2;
+        p.w_h = nb2;
+        p.w_by_head = 0;
     }
-#undef MI_SEL_WAVE
-    return hipGetLastError();
+    p.block_idx = a.block_idx;
+    p.block_count = a.block_count;
+    const int T32 = (p.nb + 31) / 32;
+    const int64_t tiles = (int64_t)a.B * a.n_heads * (T32 * (T32 + 1) / 2);
+    const dim3 grid((unsigned)((tiles + kAdWaves - 1) / kAdWaves)), block(64 * kAdWaves);
+    if (a.dtype == MI_BF16) {
+        if (a.D == 64) hipLaunchKernelGGL((ad_scores<uint16_t, 64>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((ad_scores<uint16_t, 128>), grid, block, 0, s, p);
+    } else {
+        if (a.D == 64) hipLaunchKernelGGL((ad_scores<float, 64>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((ad_scores<float, 128>), grid, block, 0, s, p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_select(p, weights, s);
 }
 
 }  // namespace mi

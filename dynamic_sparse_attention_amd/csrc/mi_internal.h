@@ -106,6 +106,10 @@ struct BsArgs {
 size_t bs_workspace_bytes(int32_t B, int32_t n_heads, int32_t Hkv, int32_t N, int32_t D,
                           bool caller_scores);
 hipError_t launch_block_estimate(const BsArgs& a, hipStream_t s);
+// Antidiagonal block scores with the same selection (BsArgs.w: caller weights
+// or NULL; ws: the score rows, ad_workspace_bytes).
+size_t ad_workspace_bytes(int32_t B, int32_t n_heads, int32_t N, bool caller_scores);
+hipError_t launch_antidiag_estimate(const BsArgs& a, hipStream_t s);
 
 struct IndexArgs {
     int32_t B, Hq, N;

@@ -11,7 +11,7 @@ set -u
 C=$1
 O=$(realpath -m "$2")
 R=$(cd "$(dirname "$0")/.." && pwd)
-B="--no-cpu-baseline --no-1m --no-dense --no-exact --no-gather"
+B="--no-cpu-baseline --no-1m --no-dense --no-exact --no-gather --no-antidiag"
 T=${PROFILE_PASS_SECONDS:-400}
 mkdir -p "$O/$C"
 cd /tmp && export TMPDIR=/tmp

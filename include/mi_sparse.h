@@ -69,7 +69,12 @@ typedef enum { MI_F32 = 0, MI_BF16 = 1 } mi_dtype;
 typedef enum { MI_ASHAPE = 0, MI_VSLASH = 1, MI_BSPARSE = 2, MI_DENSE = 3, MI_VSLASH_EXACT = 4 } mi_pattern;
 
 /* Workspace-sized operations for mi_workspace_bytes(). */
-typedef enum { MI_OP_VS_ESTIMATE = 0, MI_OP_BLOCK_ESTIMATE = 1, MI_OP_SPARSE_PREFILL = 2 } mi_op;
+typedef enum {
+    MI_OP_VS_ESTIMATE = 0,
+    MI_OP_BLOCK_ESTIMATE = 1,
+    MI_OP_SPARSE_PREFILL = 2,
+    MI_OP_ANTIDIAG_ESTIMATE = 3
+} mi_op;
 
 typedef struct {
     int32_t batch, heads_q, heads_kv, seq_len, head_dim; /* head_dim in {64, 128} */
@@ -106,7 +111,8 @@ typedef struct {
 } mi_index;
 
 /* Bytes of workspace an operation needs.  op = MI_OP_VS_ESTIMATE: p0 = number
- * of listed heads; MI_OP_BLOCK_ESTIMATE: p0 = number of listed heads;
+ * of listed heads; MI_OP_BLOCK_ESTIMATE and MI_OP_ANTIDIAG_ESTIMATE: p0 = number
+ * of listed heads;
  * MI_OP_SPARSE_PREFILL: the attention item schedule, which mi_sparse_prefill
  * builds in ws with a kernel on the stream before the attention reads it
  * (optional: with ws = NULL the attention uses its default order).  Returns
@@ -165,12 +171,34 @@ mi_status mi_vs_estimate(const mi_attn_desc* desc, const void* q, const void* k,
  *                nb <= 512 the scores z stay on chip as well (one fused
  *                kernel); longer rows keep z in ws between two kernels
  *   ws           >= mi_workspace_bytes(desc, MI_OP_BLOCK_ESTIMATE, n_heads, 0)
- * Requires top_blocks >= 2.  Equal weights rank the lower block first; the
- * lists do not depend on whether block_score is given. */
+ * Requires top_blocks >= 2 and 16-byte aligned q and k.  Equal weights rank
+ * the lower block first; the lists do not depend on whether block_score is
+ * given. */
 mi_status mi_block_estimate(const mi_attn_desc* desc, const void* q, const void* k,
                             const int32_t* heads, int32_t n_heads, int32_t top_blocks,
                             int32_t* block_idx, int32_t* block_count, float* block_score,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Block-Sparse index from antidiagonal block scores (hysenlabs review of the
+ * MInference repository, "How MInference differs from xAttention, FlexPrefill
+ * and RetrievalAttention": xAttention scores blocks by antidiagonal sums to
+ * decide which to keep).  The score of query block a and key block c is the
+ * sum of the scaled logits along the 64x64 block's main antidiagonal,
+ *   x[a, c] = scale * sum_{r<64} q[64a + r] . k[64c + 63 - r]   for c < a,
+ * and over its causal half (r >= 32) for c = a; weights and lists then follow
+ * mi_block_estimate: w = softmax over c <= a of x, block_idx[a] = {0, a} plus
+ * the highest-weight other causal blocks, min(top_blocks, a + 1) in total,
+ * ascending, padded with -1.  The output lists feed mi_build_index as
+ * MI_BSPARSE lists.
+ *   heads, block_idx, block_count, block_score: as for mi_block_estimate
+ *   ws   >= mi_workspace_bytes(desc, MI_OP_ANTIDIAG_ESTIMATE, n_heads, 0): the
+ *        score rows [batch, n_heads, nb, nb] fp32 (256 bytes when block_score
+ *        is given: the scores are then formed in block_score itself)
+ * Requires top_blocks >= 2.  Errors as for mi_block_estimate. */
+mi_status mi_antidiag_estimate(const mi_attn_desc* desc, const void* q, const void* k,
+                               const int32_t* heads, int32_t n_heads, int32_t top_blocks,
+                               int32_t* block_idx, int32_t* block_count, float* block_score,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Conversion of the estimates into per-query-block work lists (aifetchly
  * guide, "1. The Vertical-Slash Kernel Mechanics": verticals are read as

@@ -115,6 +115,26 @@ def test_block_estimate_validation():
                                1 << 40, None) == 2
 
 
+def test_antidiag_estimate_validation():
+    l = mi.lib()
+    d = desc()
+    # every call below fails validation, so nothing is launched on the fake pointers
+    call = lambda top=4, ws_bytes=1 << 30, bidx=FAKE, q=FAKE: l.mi_antidiag_estimate(
+        ctypes.byref(d), q, FAKE, heads(0, 2), 2, top, bidx, FAKE, None, FAKE, ws_bytes, None)
+    assert call(top=1) == 3
+    assert call(ws_bytes=8) == 5
+    assert call(bidx=None) == 1
+    assert call(q=FAKE + 8) == 2  # 16-byte alignment
+    # the score rows live in the workspace unless the caller passes block_score
+    nb = 1024 // 64
+    need = l.mi_workspace_bytes(ctypes.byref(d), mi.OP_ANTIDIAG_ESTIMATE, 2, 0)
+    assert need >= 2 * nb * nb * 4
+    assert call(ws_bytes=need - 1) == 5
+    long = desc(seq_len=64 * 40000)
+    assert l.mi_antidiag_estimate(ctypes.byref(long), FAKE, FAKE, heads(0), 1, 4, FAKE, FAKE, None, FAKE,
+                                  1 << 40, None) == 2
+
+
 def index_struct(bcap=32, ccap=16, cols=True, bits=False):
     s = mi.MiIndex()
     s.block_count, s.block_idx = FAKE, FAKE

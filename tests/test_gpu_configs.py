@@ -265,6 +265,33 @@ def test_c2_block_sparse_gqa():
                 att_blocks=blocks)
 
 
+def test_antidiag_estimate_32k():
+    """Antidiagonal block scores on the 32K block-sparse layer: the weights of
+    every causal block and the list of every row of two heads (one per kv
+    group of the planted hot blocks) against the fp64 oracle."""
+    w = W.C2
+    nb = w.n_blocks
+    say(f"{w.name}: antidiagonal estimate")
+    data = W.generate(w, with_v=False)
+    dev = torch.device("cuda")
+    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k = up(data["q"]), up(data["k"])
+    heads = [0, 9]
+    bidx, bcnt, gw = mi.antidiag_estimate(q, k, heads, w.top_blocks)
+    torch.cuda.synchronize()
+    tri = np.tril(np.ones((nb, nb), bool))
+    for h in heads:
+        g = gw[0, h].double().cpu().numpy()
+        bi, bc = bidx[0, h].cpu().numpy(), bcnt[0, h].cpu().numpy()
+        rw, _ = O.antidiag_estimate(W.to_f64(data["q"][0, h], w.dtype), W.to_f64(data["k"][0, h // w.group], w.dtype),
+                                    w.scale, w.top_blocks)
+        assert_scores_close(g[tri], rw[tri], f"antidiagonal weights h{h}")
+        for a in range(nb):
+            kk = min(w.top_blocks, a + 1)
+            assert bc[a] == kk
+            check_selection(bi[a], g[a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"antidiag h{h} a{a}")
+
+
 @pytest.mark.timeout(600)
 def test_c3_vertical_slash_128k():
     w = W.C3

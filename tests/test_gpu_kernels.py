@@ -420,3 +420,73 @@ def test_exact_vertical_slash_needs_maps():
     with pytest.raises(mi.MiError) as e:
         mi.sparse_prefill(q, q, q, [W.VSLASH_EXACT], idx)
     assert e.value.status == 1 and "vs_bits" in str(e.value)
+
+
+# ----------------------------------------------------------------- antidiagonal block scores
+
+@pytest.mark.parametrize("dtype,d,n,top", [("bf16", 128, 64 * 40, 6), ("f32", 64, 64 * 9, 3),
+                                           ("bf16", 64, 64 * 70, 2), ("bf16", 128, 64 * 33, 100),
+                                           ("f32", 128, 64 * 37, 5)])
+def test_antidiag_estimate(dtype, d, n, top):
+    """Weights of every causal block and every row's list against the fp64
+    oracle; the lists are the same when the weights are not stored; heads
+    not listed are left alone."""
+    say(f"antidiag_estimate {dtype} d={d} n={n} top={top}")
+    hq, hkv = 4, 2
+    _, (q, k, _), (q64, k64, _) = _inputs(31, hq, hkv, n, d, dtype, std=0.5)
+    heads = [1, 2]
+    bidx, bcnt, w = mi.antidiag_estimate(q, k, heads, top)
+    nidx, ncnt, none = mi.antidiag_estimate(q, k, heads, top, return_scores=False)
+    torch.cuda.synchronize()
+    assert none is None
+    bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    assert np.array_equal(nidx.cpu().numpy(), bidx) and np.array_equal(ncnt.cpu().numpy(), bcnt)
+    nb = n // 64
+    tri = np.tril(np.ones((nb, nb), bool))
+    for h in heads:
+        rw, _ = O.antidiag_estimate(q64[0, h], k64[0, h // 2], d ** -0.5, top)
+        assert_scores_close(w[0, h][tri], rw[tri], f"antidiagonal weights h{h}")
+        assert not w[0, h][~tri].any()
+        for a in range(nb):
+            kk = min(top, a + 1)
+            assert bcnt[0, h, a] == kk
+            check_selection(bidx[0, h, a], w[0, h, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"antidiag h{h} a{a}")
+    assert not bcnt[0, 0].any() and not bcnt[0, 3].any()
+
+
+@pytest.mark.parametrize("nb", [129, 513, 1025, 2049])
+def test_antidiag_long_rows(nb):
+    """Every row of layers on each side of the selection's dispatch
+    boundaries (register slots per lane 8, 16, 32, 64)."""
+    say(f"antidiag_estimate long rows nb={nb}")
+    n, d, top = 64 * nb, 64, 20
+    _, (q, k, _), (q64, k64, _) = _inputs(32, 1, 1, n, d, "bf16", std=0.5)
+    bidx, bcnt, w = mi.antidiag_estimate(q, k, [0], top)
+    torch.cuda.synchronize()
+    bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    rw, _ = O.antidiag_estimate(q64[0, 0], k64[0, 0], d ** -0.5, top)
+    tri = np.tril(np.ones((nb, nb), bool))
+    assert_scores_close(w[0, 0][tri], rw[tri], "antidiagonal weights")
+    for a in range(nb):
+        kk = min(top, a + 1)
+        assert bcnt[0, 0, a] == kk
+        check_selection(bidx[0, 0, a], w[0, 0, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"antidiag a{a}")
+
+
+def test_antidiag_lists_drive_the_attention():
+    """Lists from the antidiagonal estimate, used as Block-Sparse lists by the
+    index and the attention, against the oracle's attention over them."""
+    say("antidiag lists -> attention")
+    n, hq, hkv, d, top = 64 * 24, 4, 2, 128, 5
+    _, (q, k, v), (q64, k64, v64) = _inputs(33, hq, hkv, n, d, "bf16", std=0.5)
+    pat = [W.BSPARSE] * hq
+    bidx, bcnt, _ = mi.antidiag_estimate(q, k, list(range(hq)), top, return_scores=False)
+    idx = mi.build_index(q, k, pat, None, None, bidx, bcnt, top)
+    o, _ = mi.sparse_prefill(q, k, v, pat, idx)
+    torch.cuda.synchronize()
+    of = f64(o)
+    for h in range(hq):
+        for a in (0, 7, 23):
+            blocks, cols = gpu_index_lists(idx, 0, h, a)
+            ref, _ = O.attention_from_index(q64[0, h], k64[0, h // 2], v64[0, h // 2], d ** -0.5, a, blocks, cols)
+            assert np.abs(of[0, h, 64 * a: 64 * a + 64] - ref).max() < BF16_ATOL, (h, a)
