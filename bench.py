@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token secondary measurement")
     ap.add_argument("--no-gather", action="store_true", help="skip the isolated column-gather rate")
     ap.add_argument("--no-antidiag", action="store_true", help="skip the antidiagonal block estimate")
+    ap.add_argument("--library-context", action="store_true",
+                    help="also time torch's bf16 GEMM and its flash SDPA (causal) at the layer's shape")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact (element-masked) Vertical-Slash variant and the clustered-slash layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -377,6 +379,57 @@ def antidiag_rate(q, k, w):
             "note": "scores as a dense contraction over 64*d per block pair (MFMA), then the block softmax and top-k"}
 
 
+def library_context(q, k, v, dense_ms):
+    """Reference points from the libraries on the same GPU (not part of the
+    path): hipBLASLt's bf16 GEMM through torch.matmul (8192^3, median of
+    three bursts of 50), and torch's flash SDPA, causal, on the layer's Q/K/V
+    with the kv heads repeated (median of three), against this library's
+    dense causal comparator on the same inputs."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def med(f, n, reps=3):
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / n)
+        return float(np.median(ts))
+
+    g = torch.Generator(device=q.device).manual_seed(7)
+    m = 8192
+    a = torch.randn(m, m, device=q.device, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(m, m, device=q.device, dtype=torch.bfloat16, generator=g)
+    ms = med(lambda: torch.matmul(a, b), 50)
+    tf = 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+    out["gemm_bf16"] = {"shape": [m, m, m], "ms": round(ms, 4), "tflops": round(tf, 1),
+                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del a, b
+    B, Hq, N, d = q.shape
+    g_ = Hq // k.shape[1]
+    kk = k.repeat_interleave(g_, dim=1).contiguous()
+    vv = v.repeat_interleave(g_, dim=1).contiguous()
+    flop = 4.0 * d * B * Hq * N * (N + 1) / 2
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms = med(lambda: torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True), 1)
+        out["sdpa_flash_causal"] = {"ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                                    "dense_comparator_ms": None if dense_ms is None else round(dense_ms, 3),
+                                    "flop": "4*d*H*N(N+1)/2"}
+    except RuntimeError as e:
+        out["sdpa_flash_causal"] = {"error": str(e)[:200]}
+    del kk, vv
+    return out
+
+
 def sampled_parity(plan, w, data, n_items=8):
     """Attention rows of the plan (relaunched on its index, since the dense
     comparator shares the output buffer) against the oracle fed the GPU's
@@ -509,6 +562,9 @@ def main():
     if not args.no_antidiag:
         log("[bench] antidiagonal block estimate")
         out["antidiag_estimate"] = antidiag_rate(plan.q, plan.k, w)
+    if args.library_context and w.dtype == "bf16":
+        log("[bench] library reference points")
+        out["library_context"] = library_context(plan.q, plan.k, plan.v, r["dense"]["ms"] if "dense" in r else None)
     if not args.no_exact and any(p == W.VSLASH for p in plan.pat):
         # the same layer with the Vertical-Slash heads element-masked to their
         # exact key sets: attention time on the same estimate and index lists

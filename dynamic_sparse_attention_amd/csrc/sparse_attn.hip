@@ -30,6 +30,11 @@
 // wavefronts sharing a SIMD keep the matrix cores and the vector ALUs busy
 // at the same time.
 //
+// Split schedule (launches whose heads are all Block-Sparse, when two lists
+// per item fit the step area): the four blocks of an item share few key
+// blocks, so each group walks the union of its own two blocks' lists with
+// its own K and V buffer; the phases stay paired by the same barriers.
+//
 // Staging: K and V rows go from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane, 1 KiB of consecutive LDS
 // per wave instruction; the head's rows are one raw buffer, the tile's first
@@ -200,9 +205,12 @@ __device__ __forceinline__ void issue_rows(char* dst, uint32_t w, const int32_t*
 // column lists) to LDS; returns the number of steps.  Sparse heads: a mask
 // byte per key block kb <= a_3 (bit i: block a_i lists kb, kb <= a_i), then
 // an ordered compaction of the non-empty masks.  Dense heads: every causal
-// key block, computed by the blocks at or after it.
+// key block, computed by the blocks at or after it.  split: two lists, one
+// per ping-pong group (key blocks that block 2g or 2g+1 lists, with those
+// two mask bits), n0 entries then n1; the caller guarantees n0 + n1 <= nb.
 template <typename T, int D>
-__device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, int a0, int nblk) {
+__device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, int a0, int nblk, bool split,
+                           int& n0, int& n1) {
     typedef Arena<T, D> A;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int cstride = p.cstride;
@@ -245,6 +253,18 @@ __device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, 
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) c += ((mine[j] >> (8 * bb)) & 0xffu) ? 1 : 0;
         }
+        if (split) {
+            // one list per ping-pong group: key blocks that block 2g or 2g+1
+            // lists, with those two mask bits; counts packed (low: group 0)
+            c = 0;
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j)
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const uint32_t m = (mine[j] >> (8 * bb)) & 0xffu;
+                    c += ((m & 3u) ? 1 : 0) + ((m & 12u) ? 0x10000 : 0);
+                }
+        }
         int incl = c;  // inclusive scan over the wavefront
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -260,14 +280,30 @@ __device__ int build_steps(char* dyn, const Params& p, int pattern, int64_t r0, 
             before += w < wv ? scan[w] : 0;
             ntiles += scan[w];
         }
-        int o = before + incl - c;
+        if (split) {
+            n0 = ntiles & 0xffff;
+            n1 = ntiles >> 16;
+            ntiles = n0 + n1;
+            int o0 = (before + incl - c) & 0xffff, o1 = n0 + ((before + incl - c) >> 16);
 #pragma unroll
-        for (int j = 0; j < kMaxPer; ++j)
+            for (int j = 0; j < kMaxPer; ++j)
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const uint32_t m = (mine[j] >> (8 * bb)) & 0xffu;
-                if (m) steps[o++] = pack_step(4 * (t * per + j) + bb, (int)m, 0, 0);
-            }
+                for (int bb = 0; bb < 4; ++bb) {
+                    const uint32_t m = (mine[j] >> (8 * bb)) & 0xffu;
+                    const int kb = 4 * (t * per + j) + bb;
+                    if (m & 3u) steps[o0++] = pack_step(kb, (int)(m & 3u), 0, 0);
+                    if (m & 12u) steps[o1++] = pack_step(kb, (int)(m & 12u), 0, 0);
+                }
+        } else {
+            int o = before + incl - c;
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j)
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const uint32_t m = (mine[j] >> (8 * bb)) & 0xffu;
+                    if (m) steps[o++] = pack_step(4 * (t * per + j) + bb, (int)m, 0, 0);
+                }
+        }
     }
     int nsteps = ntiles;
     if (pattern == MI_VSLASH || pattern == MI_VSLASH_EXACT) {
@@ -720,7 +756,7 @@ __device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); 
 // EXACT: the instantiation launched when some head is MI_VSLASH_EXACT (its
 // tile steps take the per-element Vertical-Slash mask); the other
 // instantiation carries no code for it.
-template <typename T, int D, bool EXACT>
+template <typename T, int D, bool EXACT, bool SPLIT>
 __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     typedef typename Elem<T>::frag Frag;
     typedef Layout<T, D> Ly;
@@ -775,12 +811,21 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
     const int64_t kstride = p.ks2 * (int64_t)sizeof(T), vstride = p.vs2 * (int64_t)sizeof(T);
 
     const int64_t r0 = (int64_t)bh * p.nb + a0;
-    const int nsteps = build_steps<T, D>(dyn, p, pattern, r0, a0, nblk);
+    // Block-Sparse items whose four lists hold at most nb entries run in
+    // split mode: each ping-pong group walks the union of its own two
+    // blocks' lists with its own K and V buffer (the four blocks' lists share
+    // few key blocks, so one common step list would leave most of its steps
+    // to a single block).
+    const bool split = SPLIT && pattern == MI_BSPARSE && 4 * p.block_cap <= p.nb;
+    int n0 = 0, n1 = 0;
+    const int nsteps = build_steps<T, D>(dyn, p, pattern, r0, a0, nblk, split, n0, n1);
     const int32_t* colsl = reinterpret_cast<const int32_t*>(dyn);
     const uint32_t* steps = reinterpret_cast<const uint32_t*>(dyn + Ar::steps(p.cstride));
     const int cstride = p.cstride;
+    const uint32_t* my_steps = (split && grp == 1) ? steps + n0 : steps;
+    const int my_n = split ? (grp == 1 ? n1 : n0) : nsteps;
     auto fetch = [&](int t) -> uint32_t {
-        return t < nsteps ? (uint32_t)__builtin_amdgcn_readfirstlane(steps[t]) : kNoStep;
+        return t < my_n ? (uint32_t)__builtin_amdgcn_readfirstlane(my_steps[t]) : kNoStep;
     };
 
     QOperand<T, D> qf;
@@ -904,6 +949,44 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
         advance(t);
         return true;
     };
+    if (split) {
+        // Phase 2t: group 0 runs M(t) on its step t, group 1 copies K of its
+        // step t and V of its step t-1, then runs V(t-1); phase 2t+1: group 0
+        // copies V of its step t and K of its step t+1, then runs V(t), group
+        // 1 runs M(t).  Group g stages into K buffer g and V buffer g only
+        // (each buffer's last reader finished in the phase before the copy)
+        // and waits for its copies at the end of the phase that issued them.
+        // Both loops run max(n0, n1) + 1 iterations of two barriers.
+        const int T2 = max(n0, n1);
+        if (wcur != kNoStep && grp == 0)
+            issue_rows<T, D>(kbuf0, wcur, nullptr, nullptr, kbase, kstride, wave & 3, 0, NI);
+        __syncthreads();
+        if (grp == 0) {
+            for (int t = 0; t <= T2; ++t) {
+                const bool pv_need = needs(wprev), s_need = needs(wcur);
+                m_phase(kbuf0, vbuf0, cpos0, pv_need, s_need, s_keep);
+                __syncthreads();
+                if (wcur != kNoStep) issue_rows<T, D>(vbuf0, wcur, nullptr, nullptr, vbase, vstride, wave & 3, 0, NI);
+                if (wnext != kNoStep)
+                    issue_rows<T, D>(kbuf0, wnext, nullptr, nullptr, kbase, kstride, wave & 3, 0, NI);
+                v_phase(s_need, s_keep);
+                __syncthreads();
+                advance(t);
+            }
+        } else {
+            for (int t = 0; t <= T2; ++t) {
+                const bool pv_need = needs(wprev), s_need = needs(wcur);
+                if (wcur != kNoStep) issue_rows<T, D>(kbuf1, wcur, nullptr, nullptr, kbase, kstride, wave & 3, 0, NI);
+                if (wprev != kNoStep)
+                    issue_rows<T, D>(vbuf1, wprev, nullptr, nullptr, vbase, vstride, wave & 3, 0, NI);
+                v_phase(pv_need, s_keep);
+                __syncthreads();
+                m_phase(kbuf1, vbuf1, cpos1, pv_need, s_need, s_keep);
+                __syncthreads();
+                advance(t);
+            }
+        }
+    } else {
     if (wcur != kNoStep && grp == 1)
         issue_rows<T, D>(kbuf0, wcur, colsl + step_blk(wcur) * cstride + step_kb(wcur), cpos0, kbase, kstride,
                          wave & 3, 0, NI);
@@ -918,6 +1001,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(Params p) {
             if (!step1(t, kbuf0, kbuf1, vbuf1, cpos0, cpos1)) break;
             if (!step1(t + 1, kbuf1, kbuf0, vbuf0, cpos1, cpos0)) break;
         }
+    }
     }
 
     if (!active) return;
@@ -951,15 +1035,15 @@ size_t lds_bytes_t(int nb, int cstride) {
     return (size_t)Arena<T, D>::kStatic + (size_t)Arena<T, D>::bytes(nb, cstride);
 }
 
-template <typename T, int D, bool EXACT>
+template <typename T, int D, bool EXACT, bool SPLIT = false>
 hipError_t launch_t(const Params& p, hipStream_t s) {
     const int items = p.sched ? p.sched_len : p.B * p.Hq * p.nruns;
     const size_t dyn = lds_bytes_t<T, D>(p.nb, p.cstride) - Arena<T, D>::kStatic;
     if (dyn + Arena<T, D>::kStatic > kAttnMaxLds) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D, EXACT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<T, D, EXACT, SPLIT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, EXACT>), dim3(items), dim3(kThreads), dyn, s, p);
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, EXACT, SPLIT>), dim3(items), dim3(kThreads), dyn, s, p);
     return hipGetLastError();
 }
 
@@ -1007,10 +1091,16 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
     for (int h = 0; h < a.Hq; ++h) any_exact |= !a.all_dense && a.pattern[h] == MI_VSLASH_EXACT;
     p.vs_bits = a.vs_bits;
     p.bits_words = a.N / 32 + 4;
+    // layers whose heads are all Block-Sparse take the split schedule
+    bool all_bs = !a.all_dense;
+    for (int h = 0; h < a.Hq; ++h) all_bs &= !a.all_dense && a.pattern[h] == MI_BSPARSE;
+    const bool split = all_bs && 4 * a.block_cap <= p.nb;
     if (a.dtype == MI_BF16) {
+        if (split) return a.D == 128 ? launch_t<uint16_t, 128, false, true>(p, s) : launch_t<uint16_t, 64, false, true>(p, s);
         if (any_exact) return a.D == 128 ? launch_t<uint16_t, 128, true>(p, s) : launch_t<uint16_t, 64, true>(p, s);
         return a.D == 128 ? launch_t<uint16_t, 128, false>(p, s) : launch_t<uint16_t, 64, false>(p, s);
     }
+    if (split) return a.D == 128 ? launch_t<float, 128, false, true>(p, s) : launch_t<float, 64, false, true>(p, s);
     if (any_exact) return a.D == 128 ? launch_t<float, 128, true>(p, s) : launch_t<float, 64, true>(p, s);
     return a.D == 128 ? launch_t<float, 128, false>(p, s) : launch_t<float, 64, false>(p, s);
 }
