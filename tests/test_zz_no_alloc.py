@@ -60,6 +60,12 @@ def test_noalloc_equals_workspace_entry_twice_then_smaller():
     q, k, v, _ = _layer(5, 4, 1, 64 * 40, [W.DENSE] * 4)
     (o1, l1), (o2, l2) = _both(q, k, v, None, None)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # all heads Block-Sparse with lists short enough for the split schedule
+    bs = [W.BSPARSE] * 4
+    q, k, v, idx = _layer(9, 4, 2, 64 * 40, bs)
+    assert 4 * idx.block_cap <= 40
+    (o1, l1), (o2, l2) = _both(q, k, v, bs, idx)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_noalloc_rejects_schedules_above_the_buffer():
