@@ -379,6 +379,40 @@ def antidiag_rate(q, k, w):
             "note": "scores as a dense contraction over 64*d per block pair (MFMA), then the block softmax and top-k"}
 
 
+def plant_recall(plan, w):
+    """Diagnostic of the synthetic plants' strength: the fraction of a kv
+    head's planted keys found among each Vertical-Slash head's selected
+    verticals (key 0 is always one of the plants), and the fraction of
+    (query block, planted hot block at or before it) pairs that the
+    Block-Sparse heads' lists select.  Not a parity check: the plants are
+    weak beside the logit noise at these lengths and are left as specified."""
+    import workloads as W
+    g = w.heads_q // w.heads_kv
+    out = {}
+    vs = [h for h, pt in enumerate(plan.pat) if pt in (W.VSLASH, W.VSLASH_EXACT)]
+    if vs and w.n_vertical_plants > 0 and plan.vidx is not None:
+        vidx = plan.vidx[0].cpu().numpy()
+        rec = [float(np.isin(W.vertical_plants(w, h // g), vidx[h]).mean()) for h in vs]
+        out["vertical"] = {"heads": len(vs), "plants_per_kv_head": int(w.n_vertical_plants),
+                           "mean_recall": round(float(np.mean(rec)), 4), "min_recall": round(min(rec), 4),
+                           "max_recall": round(max(rec), 4)}
+    bs = [h for h, pt in enumerate(plan.pat) if pt == W.BSPARSE]
+    if bs and w.n_hot_blocks > 0 and plan.bidx is not None:
+        bidx = plan.bidx[0].cpu().numpy()
+        bcnt = plan.bcnt[0].cpu().numpy()
+        nb = bidx.shape[1]
+        hits = elig = 0
+        for h in bs:
+            hot = np.zeros(nb, bool)
+            hot[W.hot_blocks(w, h // g)] = True
+            valid = np.arange(bidx.shape[2])[None, :] < bcnt[h][:, None]
+            hits += int((hot[np.clip(bidx[h], 0, nb - 1)] & valid).sum())
+            elig += int(np.cumsum(hot).sum())
+        out["hot_blocks"] = {"heads": len(bs), "hot_blocks_per_kv_head": int(w.n_hot_blocks),
+                             "recall": round(hits / max(elig, 1), 4)}
+    return out
+
+
 def library_context(q, k, v, dense_ms):
     """Reference points from the libraries on the same GPU (not part of the
     path): hipBLASLt's bf16 GEMM through torch.matmul (8192^3, median of
@@ -550,6 +584,7 @@ def main():
     }
     if "dense" in r:
         out["dense_comparator"] = r["dense"]
+    out["plant_recall"] = plant_recall(plan, w)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, data, plan, args.cpu_seconds)
@@ -616,6 +651,7 @@ def main():
         if "dense" in r5:
             out["secondary"]["dense_comparator"] = r5["dense"]
             out["secondary"]["speedup_vs_dense_attention"] = round(r5["dense"]["ms"] / r5["ms_step"], 3)
+        out["secondary"]["plant_recall"] = plant_recall(plan5, w5)
         del plan5
     print(json.dumps(out), flush=True)
 

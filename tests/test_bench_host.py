@@ -46,3 +46,34 @@ def test_exact_pairs_match_brute_force():
     want = (brute(W.ASHAPE, N, sink=16, local=40) + brute(W.VSLASH, N, V=set(V), S=set(S)) +
             brute(W.BSPARSE, N, kept=kept) + brute(W.DENSE, N))
     assert got == want
+
+
+def test_plant_recall_counts_planted_keys_and_hot_blocks():
+    """The recall diagnostic on hand-made selections: every hot block at or
+    before a query block selected gives 1; half of each kv head's planted
+    keys among a Vertical-Slash head's verticals gives 0.5."""
+    import types
+    import torch
+    w = W.WORKLOADS["c2"]
+    nb, g = w.n_blocks, w.heads_q // w.heads_kv
+    bidx = np.full((1, w.heads_q, nb, w.top_blocks), -1, np.int32)
+    bcnt = np.zeros((1, w.heads_q, nb), np.int32)
+    for h in range(w.heads_q):
+        hot = W.hot_blocks(w, h // g)
+        for a in range(nb):
+            sel = hot[hot <= a]
+            bidx[0, h, a, :len(sel)] = sel
+            bcnt[0, h, a] = len(sel)
+    plan = types.SimpleNamespace(pat=[W.BSPARSE] * w.heads_q, vidx=None,
+                                 bidx=torch.from_numpy(bidx), bcnt=torch.from_numpy(bcnt))
+    assert bench.plant_recall(plan, w)["hot_blocks"]["recall"] == 1.0
+    bcnt[:] = 0  # nothing selected
+    assert bench.plant_recall(plan, w)["hot_blocks"]["recall"] == 0.0
+    w3 = W.WORKLOADS["c3"]
+    vidx = np.full((1, w3.heads_q, w3.n_vertical), -1, np.int32)
+    for h in range(w3.heads_q):
+        pl = W.vertical_plants(w3, h // (w3.heads_q // w3.heads_kv))
+        vidx[0, h, :len(pl) // 2] = pl[: len(pl) // 2]
+    plan = types.SimpleNamespace(pat=[W.VSLASH] * w3.heads_q, vidx=torch.from_numpy(vidx), bidx=None, bcnt=None)
+    r = bench.plant_recall(plan, w3)["vertical"]
+    assert r["mean_recall"] == r["min_recall"] == r["max_recall"] == 0.5
