@@ -256,7 +256,12 @@ mi_status mi_build_index(const mi_attn_desc* desc, const int32_t* head_pattern,
  *        small kernel that writes the item schedule of mi_attn_schedule()
  *        into ws, and the attention runs its work items in that order (the
  *        results are bit-identical either way).  ws is overwritten by every
- *        call; two calls sharing it on different streams race. */
+ *        call; two calls sharing it on different streams race.
+ * A launch whose heads are all MI_BSPARSE, with 4 * idx->block_cap <= nb,
+ * runs a schedule in which each half of a work item walks its own two
+ * blocks' lists; its results are bit-identical to the common schedule's.
+ * The call enqueues kernels only (no memset, copy or allocation), so it may
+ * be captured in a HIP graph. */
 mi_status mi_sparse_prefill(const mi_attn_desc* desc, const void* q, const void* k,
                             const void* v, const int32_t* head_pattern, const mi_index* idx,
                             int32_t sink_tokens, int32_t local_tokens, void* o, float* lse,
