@@ -611,58 +611,59 @@ __global__ void __launch_bounds__(64 * kAdWaves) ad_scores(BsP p) {
     }
 }
 
-// bf16: one workgroup of eight wavefronts per 128 x 128 tile of X (query
-// blocks 128 ta + i, key blocks 128 tc + j, tc <= ta), which reads four
-// times fewer operand rows per product than a wavefront per 32 x 32 tile.
-// For each r the 128 query rows 64a + r and the 128 key rows 64c + 63 - r go
-// global -> LDS (double-buffered; 16-byte chunk c of row y stored at chunk
-// c ^ (y % 16), so the fragment reads of 32 consecutive rows hit distinct
-// banks); wavefront w computes key blocks 32 (w % 4) .. + 31 against query
-// blocks 64 (w / 4) .. + 63 (two 32 x 32 products per dimension slice).
-constexpr int kAdlWaves = 8;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D>
+// bf16: one workgroup of eight wavefronts per 256 x 256 tile of X (query
+// blocks 256 ta + i, key blocks 256 tc + j, tc <= ta), which reads 16 times
+// fewer operand rows per product than a wavefront per 32 x 32 tile.  Each step
+// stages 64 dimensions of one row of each of the tile's 256 query blocks
+// (row r) and 256 key blocks (row 63 - r): 2 x 256 rows of 128 bytes,
+// global -> LDS, double-buffered; 16-byte chunk c of row y sits at c ^
+// ((y / 2) % 8), so that 16 lanes reading one chunk of 16 consecutive rows
+// hit all 64 banks once.  Wavefront w computes query blocks 64 (w / 2) ..
+// + 63 against key blocks 128 (w % 2) .. + 127: eight 32 x 32 MFMA tiles, the
+// four K operands of a slice used twice and the two Q operands four times.
+constexpr int kAdlWaves = 8;
 struct AdTile {
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kCpr = kRowBytes / 16;  // 16-byte chunks per row
-    static constexpr int kSwz = kCpr < 16 ? kCpr - 1 : 15;
-    static constexpr int kBytes = 128 * kRowBytes;  // one side (128 rows)
-    __device__ static int offset(int y, int c) { return y * kRowBytes + ((c ^ (y & kSwz)) << 4); }
+    static constexpr int kRowBytes = 128;  // 64 bf16 dimensions
+    static constexpr int kRows = 256;
+    static constexpr int kBytes = kRows * kRowBytes;  // one side
+    __device__ static int offset(int y, int c) { return y * kRowBytes + ((c ^ ((y >> 1) & 7)) << 4); }
 };
 
-// Copies of step r of ad_scores_lds into `dst` (q side, then k side): 2 sides
-// x 128 rows x kCpr chunks, one 16-byte chunk per lane per instruction; lane
-// slot (side, row y, position) takes source chunk position ^ (y % 16).  Rows
-// past nb read block nb - 1 (their scores are not written).
-template <int D>
+// Copies of step (r, half) into `dst`: 2 sides x 256 rows x 8 chunks, one
+// 16-byte chunk per lane per instruction; rows past nb read block nb - 1
+// (their scores are not written).
 __device__ __forceinline__ void ad_issue(char* dst, const uint16_t* qb, const uint16_t* kb, int64_t qs2, int64_t ks2,
-                                         int qrow0, int krow0, int nb, int r, int wv, int lane) {
-    typedef AdTile<D> At;
-    constexpr int kChunks = 2 * 128 * At::kCpr;
+                                          int qrow0, int krow0, int nb, int r, int half, int wv, int lane) {
+    constexpr int kChunks = 2 * AdTile::kRows * 8;
     constexpr int kIters = kChunks / (64 * kAdlWaves);
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int idx = it * kAdlWaves + wv;  // wave instruction index
         const int cidx = idx * 64 + lane;     // chunk slot
-        const int side = cidx / (128 * At::kCpr);
-        const int rem = cidx % (128 * At::kCpr);
-        const int y = rem / At::kCpr, pos = rem % At::kCpr;
+        const int side = cidx / (AdTile::kRows * 8);
+        const int rem = cidx % (AdTile::kRows * 8);
+        const int y = rem >> 3, pos = rem & 7;
         const int blk = min((side ? krow0 : qrow0) + y, nb - 1);
         const uint16_t* src = side ? kb + ((int64_t)blk * 64 + 63 - r) * ks2 : qb + ((int64_t)blk * 64 + r) * qs2;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + 16 * (pos ^ (y & At::kSwz)),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + 128 * half + 16 * (pos ^ ((y >> 1) & 7)),
                                          (lds_void*)(dst + idx * 1024), 16, 0, 0);
     }
 }
 
 template <int D>
 __global__ void __launch_bounds__(64 * kAdlWaves) ad_scores_lds(BsP p) {
-    typedef AdTile<D> At;
-    __shared__ __attribute__((aligned(16))) char buf[2][2][At::kBytes];  // [buffer][q, k]
-    const int T128 = (p.nb + 127) / 128;
-    const int per = T128 * (T128 + 1) / 2;
-    const int bl = blockIdx.x / per;
-    int x = blockIdx.x % per;
+    constexpr int H = D / 64;  // steps per antidiagonal row
+    __shared__ __attribute__((aligned(16))) char buf[2][2][AdTile::kBytes];  // [buffer][q, k]
+    const int T256 = (p.nb + 255) / 256;
+    const int per = T256 * (T256 + 1) / 2;
+    // consecutive tiles (of one head, sharing query and key rows) on one XCD:
+    // the hardware deals workgroups to the eight XCDs in turn
+    const int G = gridDim.x;
+    const int L = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int bl = L / per;
+    int x = L % per;
     int ta = 0;
     while (x >= ta + 1) {
         x -= ta + 1;
@@ -675,59 +676,71 @@ __global__ void __launch_bounds__(64 * kAdlWaves) ad_scores_lds(BsP p) {
     const int rl = lane & 31, hl = lane >> 5;
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + b * p.qs0 + h * p.qs1;
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + b * p.ks0 + (h / p.group) * p.ks1;
-    const int qrow0 = 128 * ta, krow0 = 128 * tc;
-    const int cs = wv & 3, as = wv >> 2;  // key sub-tile (32 blocks), query half (64 blocks)
-    f32x16 acc[2];
+    const int qrow0 = 256 * ta, krow0 = 256 * tc;
+    const int qsub = wv >> 1, khalf = wv & 1;
+    f32x16 acc[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
-    // diagonal entries: sub-tile j of this wave covers query blocks
-    // 64 as + 32 j .. + 31; it meets the key sub-tile on the diagonal when
-    // ta == tc and 2 as + j == cs
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
+    // diagonal entries (ta == tc): query sub-tile j meets key sub-tile i on
+    // the diagonal when 64 qsub + 32 j == 128 khalf + 32 i
     const int e_d = ((rl >> 3) << 2) | (rl & 3);
     const bool lane_d = ((rl >> 2) & 1) == hl;
     float d_low[2] = {0.f, 0.f};
-    ad_issue<D>(&buf[0][0][0], qb, kb, p.qs2, p.ks2, qrow0, krow0, p.nb, 0, wv, lane);
+    ad_issue(&buf[0][0][0], qb, kb, p.qs2, p.ks2, qrow0, krow0, p.nb, 0, 0, wv, lane);
 #pragma unroll 1
-    for (int r = 0; r < 64; ++r) {
-        __syncthreads();  // copies of r have landed (each wave waited for its own); r-1 is read
-        if (r + 1 < 64) ad_issue<D>(&buf[(r + 1) & 1][0][0], qb, kb, p.qs2, p.ks2, qrow0, krow0, p.nb, r + 1, wv, lane);
-        const char* qs = &buf[r & 1][0][0];
-        const char* ks = &buf[r & 1][1][0];
+    for (int st = 0; st < 64 * H; ++st) {
+        __syncthreads();  // copies of st have landed (each wave waited for its own); st-1 is read
+        if (st + 1 < 64 * H)
+            ad_issue(&buf[(st + 1) & 1][0][0], qb, kb, p.qs2, p.ks2, qrow0, krow0, p.nb, (st + 1) / H, (st + 1) % H,
+                      wv, lane);
+        const char* qs = &buf[st & 1][0][0];
+        const char* ks = &buf[st & 1][1][0];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                             ks + At::offset(32 * cs + rl, 2 * s + hl)));
+        for (int sl = 0; sl < 4; ++sl) {
+            bf16x8 kf[4], qf[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                                 qs + At::offset(64 * as + 32 * j + rl, 2 * s + hl)));
-                mma32(acc[j], kf, qf);
-            }
-        }
-        if (r == 31 && ta == tc && lane_d) {
+            for (int i = 0; i < 4; ++i)
+                kf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        ks + AdTile::offset(128 * khalf + 32 * i + rl, 2 * sl + hl)));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                if (2 * as + j == cs) {
+                qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        qs + AdTile::offset(64 * qsub + 32 * j + rl, 2 * sl + hl)));
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (e == e_d) d_low[j] = acc[j][e];
-                }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mma32(acc[j][i], kf[i], qf[j]);
+        }
+        if (st == 32 * H - 1 && ta == tc && lane_d) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (64 * qsub + 32 * j == 128 * khalf + 32 * i) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            if (e == e_d) d_low[j] = acc[j][i][e];
+                    }
         }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int a = 128 * ta + 64 * as + 32 * j + rl;
+        const int a = 256 * ta + 64 * qsub + 32 * j + rl;
         if (a >= p.nb) continue;
         float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? h : li) * p.w_h + (int64_t)a * p.nb;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = 128 * tc + 32 * cs + 8 * (e >> 2) + 4 * hl + (e & 3);
-            if (c > a || c >= p.nb) continue;
-            const float v = (c == a) ? acc[j][e] - d_low[j] : acc[j][e];
-            W[c] = v * p.scale;
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int c = 256 * tc + 128 * khalf + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+                if (c > a || c >= p.nb) continue;
+                const float v = (c == a) ? acc[j][i][e] - d_low[j] : acc[j][i][e];
+                W[c] = v * p.scale;
+            }
     }
 }
 
@@ -885,8 +898,8 @@ hipError_t launch_antidiag_estimate(const BsArgs& a, hipStream_t s) {
     const int64_t tiles = (int64_t)a.B * a.n_heads * (T32 * (T32 + 1) / 2);
     const dim3 grid((unsigned)((tiles + kAdWaves - 1) / kAdWaves)), block(64 * kAdWaves);
     if (a.dtype == MI_BF16) {
-        const int T128 = (p.nb + 127) / 128;
-        const dim3 lgrid((unsigned)(a.B * a.n_heads * (T128 * (T128 + 1) / 2))), lblock(64 * kAdlWaves);
+        const int T256 = (p.nb + 255) / 256;
+        const dim3 lgrid((unsigned)(a.B * a.n_heads * (T256 * (T256 + 1) / 2))), lblock(64 * kAdlWaves);
         if (a.D == 64) hipLaunchKernelGGL((ad_scores_lds<64>), lgrid, lblock, 0, s, p);
         else hipLaunchKernelGGL((ad_scores_lds<128>), lgrid, lblock, 0, s, p);
     } else {
