@@ -494,36 +494,37 @@ def test_antidiag_lists_drive_the_attention():
 
 # ----------------------------------------------------------------- split schedule
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
-def test_block_sparse_split_schedule(dtype, d):
+@pytest.mark.parametrize("dtype,d,batch", [("bf16", 128, 1), ("f32", 64, 1), ("bf16", 64, 1), ("bf16", 128, 2)])
+def test_block_sparse_split_schedule(dtype, d, batch):
     """Launches whose heads are all Block-Sparse, with lists short enough for
     two per item (4 * block_cap <= nb), run one step list per ping-pong group.
     Random lists of uneven length (group 0's blocks long, group 1's short, and
     the reverse on other heads) over a ragged number of blocks: every query
     block against the oracle, and bit for bit against the joint schedule that
     the same lists stored with a larger capacity select."""
-    say(f"split schedule {dtype} d={d}")
+    say(f"split schedule {dtype} d={d} batch={batch}")
     hq, hkv, n = 4, 2, 64 * 43
     nb = n // 64
-    _, (q, k, v), (q64, k64, v64) = _inputs(21, hq, hkv, n, d, dtype)
+    _, (q, k, v), (q64, k64, v64) = _inputs(21, hq, hkv, n, d, dtype, batch=batch)
     rng = np.random.default_rng(5)
     cap = nb // 4
     lists = {}
-    for h in range(hq):
-        for a in range(nb):
-            long_grp = (a % 4) // 2 == h % 2
-            kk = min(a + 1, cap if long_grp else int(rng.integers(1, 3)))
-            rest = rng.choice(a, kk - 1, replace=False) if a > 0 and kk > 1 else np.zeros(0, np.int64)
-            lists[h, a] = np.sort(np.concatenate([[a], rest])).astype(np.int64)
+    for b in range(batch):
+        for h in range(hq):
+            for a in range(nb):
+                long_grp = (a % 4) // 2 == (h + b) % 2
+                kk = min(a + 1, cap if long_grp else int(rng.integers(1, 3)))
+                rest = rng.choice(a, kk - 1, replace=False) if a > 0 and kk > 1 else np.zeros(0, np.int64)
+                lists[b, h, a] = np.sort(np.concatenate([[a], rest])).astype(np.int64)
     outs = []
     for bcap in (cap, nb):
         assert (4 * bcap <= nb) == (bcap == cap)
-        idx = mi.alloc_index(1, hq, n, bcap, 0, "cuda")
-        bc = np.zeros((1, hq, nb), np.int32)
-        bi = -np.ones((1, hq, nb, bcap), np.int32)
-        for (h, a), bl in lists.items():
-            bc[0, h, a] = len(bl)
-            bi[0, h, a, :len(bl)] = bl
+        idx = mi.alloc_index(batch, hq, n, bcap, 0, "cuda")
+        bc = np.zeros((batch, hq, nb), np.int32)
+        bi = -np.ones((batch, hq, nb, bcap), np.int32)
+        for (b, h, a), bl in lists.items():
+            bc[b, h, a] = len(bl)
+            bi[b, h, a, :len(bl)] = bl
         idx.block_count.copy_(torch.from_numpy(bc))
         idx.block_idx.copy_(torch.from_numpy(bi))
         outs.append(mi.sparse_prefill(q, k, v, [W.BSPARSE] * hq, idx))
@@ -532,12 +533,12 @@ def test_block_sparse_split_schedule(dtype, d):
     assert torch.equal(o_split, o_joint) and torch.equal(l_split, l_joint)
     of, lf = f64(o_split), f64(l_split)
     atol = F32_ATOL if dtype == "f32" else BF16_ATOL
-    for (h, a), bl in lists.items():
-        ref, rlse = O.attention_from_index(q64[0, h], k64[0, h // 2], v64[0, h // 2], d ** -0.5, a, bl,
+    for (b, h, a), bl in lists.items():
+        ref, rlse = O.attention_from_index(q64[b, h], k64[b, h // 2], v64[b, h // 2], d ** -0.5, a, bl,
                                            np.zeros(0, np.int64))
         rows = slice(64 * a, 64 * a + 64)
-        assert np.abs(of[0, h, rows] - ref).max() < atol, (h, a)
-        assert np.abs(lf[0, h, rows] - rlse).max() < 1e-3, (h, a)
+        assert np.abs(of[b, h, rows] - ref).max() < atol, (b, h, a)
+        assert np.abs(lf[b, h, rows] - rlse).max() < 1e-3, (b, h, a)
 
 
 # ----------------------------------------------------------------- graph capture
