@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-antidiag", action="store_true", help="skip the antidiagonal block estimate")
     ap.add_argument("--library-context", action="store_true",
                     help="also time torch's bf16 GEMM and its flash SDPA (causal) at the layer's shape")
+    ap.add_argument("--dense-sweep", action="store_true",
+                    help="also time the dense causal comparator and torch's flash SDPA over sequence lengths")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact (element-masked) Vertical-Slash variant and the clustered-slash layer")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -464,6 +466,54 @@ def library_context(q, k, v, dense_ms):
     return out
 
 
+def dense_sweep(lengths=(16384, 32768, 65536, 131072, 262144), hq=32, hkv=8, d=128):
+    """The dense causal comparator (this library, no index) and torch's flash
+    SDPA (kv heads repeated) on seeded N(0,1) bf16 inputs over sequence
+    lengths: median of three launches each, TFLOP/s on 4*d*H*N(N+1)/2."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import dynamic_sparse_attention_amd as mi
+    stream = torch.cuda.current_stream()
+
+    def med(f, reps=3):
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    rows = []
+    for n in lengths:
+        g = torch.Generator(device="cuda").manual_seed(n)
+        q = torch.randn(1, hq, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        k = torch.randn(1, hkv, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        v = torch.randn(1, hkv, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        o = torch.empty_like(q)
+        flop = 4.0 * d * hq * n * (n + 1) / 2
+        ours = med(lambda: mi.sparse_prefill(q, k, v, None, None, out=o, return_lse=False, schedule=True))
+        row = {"seq_len": n, "ours_ms": round(ours, 3), "ours_tflops": round(flop / ours / 1e9, 1)}
+        kk = k.repeat_interleave(hq // hkv, dim=1).contiguous()
+        vv = v.repeat_interleave(hq // hkv, dim=1).contiguous()
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                lib = med(lambda: torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True))
+            row.update({"sdpa_ms": round(lib, 3), "sdpa_tflops": round(flop / lib / 1e9, 1),
+                        "ratio": round(lib / ours, 3)})
+        except RuntimeError as e:
+            row["sdpa_error"] = str(e)[:120]
+        rows.append(row)
+        log(f"[bench] dense sweep N={n}: {row}")
+        del q, k, v, o, kk, vv
+        torch.cuda.empty_cache()
+    return rows
+
+
 def sampled_parity(plan, w, data, n_items=8):
     """Attention rows of the plan (relaunched on its index, since the dense
     comparator shares the output buffer) against the oracle fed the GPU's
@@ -597,6 +647,9 @@ def main():
     if not args.no_antidiag:
         log("[bench] antidiagonal block estimate")
         out["antidiag_estimate"] = antidiag_rate(plan.q, plan.k, w)
+    if args.dense_sweep:
+        log("[bench] dense causal attention over sequence lengths")
+        out["dense_sweep"] = dense_sweep()
     if args.library_context and w.dtype == "bf16":
         log("[bench] library reference points")
         out["library_context"] = library_context(plan.q, plan.k, plan.v, r["dense"]["ms"] if "dense" in r else None)
