@@ -80,3 +80,33 @@ def test_noalloc_rejects_schedules_above_the_buffer():
     with pytest.raises(mi.MiError) as e:
         mi.sparse_prefill_noalloc(q, k, k, None, None, out=o)
     assert e.value.status == 5 and "built-in buffer" in str(e.value)
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free entry point captured in a HIP graph (the callers it
+    is for) and replayed three times, the outputs overwritten between replays:
+    every replay equals the eager call bit for bit."""
+    pat = [W.VSLASH, W.ASHAPE, W.BSPARSE, W.DENSE]
+    q, k, v, idx = _layer(13, 4, 2, 64 * 50, pat)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 4, 64 * 50), dtype=torch.float32, device="cuda")
+    mi.sparse_prefill_noalloc(q, k, v, pat, idx, sink=100, local=600, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mi.sparse_prefill_noalloc(q, k, v, pat, idx, sink=100, local=600, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mi.sparse_prefill_noalloc(q, k, v, pat, idx, sink=100, local=600, out=o, lse=lse)
+    for rep in range(3):
+        say(f"noalloc graph replay {rep}")
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), rep
