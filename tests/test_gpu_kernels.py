@@ -30,7 +30,8 @@ def _inputs(seed, hq, hkv, n, d, dtype, batch=1, std=1.0):
 # ----------------------------------------------------------------- dense
 
 @pytest.mark.parametrize("dtype,d,n,hq,hkv", [("f32", 64, 256, 2, 1), ("bf16", 128, 512, 4, 2),
-                                              ("bf16", 64, 192, 3, 3), ("f32", 128, 128, 2, 2)])
+                                              ("bf16", 64, 192, 3, 3), ("f32", 128, 128, 2, 2),
+                                              ("bf16", 128, 64, 2, 1)])  # one query block
 def test_dense_attention(dtype, d, n, hq, hkv):
     say(f"dense {dtype} d={d} n={n} hq={hq} hkv={hkv}")
     _, (q, k, v), (q64, k64, v64) = _inputs(1, hq, hkv, n, d, dtype)
@@ -426,7 +427,7 @@ def test_exact_vertical_slash_needs_maps():
 
 @pytest.mark.parametrize("dtype,d,n,top", [("bf16", 128, 64 * 40, 6), ("f32", 64, 64 * 9, 3),
                                            ("bf16", 64, 64 * 70, 2), ("bf16", 128, 64 * 33, 100),
-                                           ("f32", 128, 64 * 37, 5)])
+                                           ("f32", 128, 64 * 37, 5), ("bf16", 128, 64, 3)])  # last: one block
 def test_antidiag_estimate(dtype, d, n, top):
     """Weights of every causal block and every row's list against the fp64
     oracle; the lists are the same when the weights are not stored; heads
