@@ -247,7 +247,8 @@ mi_status mi_build_index(const mi_attn_desc* desc, const int32_t* head_pattern,
  *              holds the block list; edges are masked per element);
  *   MI_DENSE : all keys j <= i (idx not read).
  * head_pattern == NULL runs every head as MI_DENSE (the dense comparator; idx
- * may then be NULL).  O is written in desc->dtype; bf16 inputs use bf16 MFMA
+ * may then be NULL).  A row whose A(i) is empty (an index with no block and
+ * no column for its query block) gets o_i = 0 and lse_i = -inf.  O is written in desc->dtype; bf16 inputs use bf16 MFMA
  * with fp32 softmax and accumulation, f32 inputs use fp32 MFMA.
  *   o    [batch, heads_q, seq_len, head_dim] with desc->o_stride
  *   lse  float [batch, heads_q, seq_len] or NULL

@@ -578,3 +578,38 @@ def test_layer_plan_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(plan.o, o_ref) and torch.equal(plan.lse, l_ref), rep
+
+
+def test_rows_with_no_keys():
+    """Query blocks whose lists are empty (possible only through a caller's own
+    index; the estimates always keep the forced keys): their rows come out
+    as zeros with log-sum-exp -inf, and the other blocks are unaffected."""
+    say("empty lists")
+    hq, hkv, n, d = 2, 1, 64 * 9, 128
+    _, (q, k, v), (q64, k64, v64) = _inputs(17, hq, hkv, n, d, "bf16")
+    nb = n // 64
+    idx = mi.alloc_index(1, hq, n, nb, 64, "cuda")
+    bc = np.zeros((1, hq, nb), np.int32)
+    bi = -np.ones((1, hq, nb, nb), np.int32)
+    empty = {(0, 3), (0, 8), (1, 0), (1, 4), (1, 5), (1, 6), (1, 7)}  # head 1's second item: no steps at all
+    for h in range(hq):
+        for a in range(nb):
+            if (h, a) not in empty:
+                bc[0, h, a] = a + 1
+                bi[0, h, a, :a + 1] = np.arange(a + 1)
+    idx.block_count.copy_(torch.from_numpy(bc))
+    idx.block_idx.copy_(torch.from_numpy(bi))
+    for pat in (W.BSPARSE, W.VSLASH):
+        o, lse = mi.sparse_prefill(q, k, v, [pat] * hq, idx)
+        torch.cuda.synchronize()
+        of, lf = f64(o), f64(lse)
+        for h in range(hq):
+            for a in range(nb):
+                rows = slice(64 * a, 64 * a + 64)
+                if (h, a) in empty:
+                    assert not of[0, h, rows].any() and np.all(np.isneginf(lf[0, h, rows])), (pat, h, a)
+                else:
+                    ref, rlse = O.attention_from_index(q64[0, h], k64[0, 0], v64[0, 0], d ** -0.5, a,
+                                                       np.arange(a + 1), np.zeros(0, np.int64))
+                    assert np.abs(of[0, h, rows] - ref).max() < BF16_ATOL, (pat, h, a)
+                    assert np.abs(lf[0, h, rows] - rlse).max() < 1e-3
