@@ -27,8 +27,8 @@ import torch
 import dynamic_sparse_attention_amd as mi
 import workloads as W
 from oracle import minference_oracle as O
-from tests.parity_util import (BF16_ATOL, F32_ATOL, assert_scores_close, check_selection, say,
-                               to_device)
+from tests.parity_util import (BF16_ATOL, F32_ATOL, assert_scores_close, check_selection,
+                               gpu_index_lists, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -290,6 +290,42 @@ def test_antidiag_estimate_32k():
             kk = min(w.top_blocks, a + 1)
             assert bc[a] == kk
             check_selection(bi[a], g[a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"antidiag h{h} a{a}")
+
+
+@pytest.mark.timeout(600)
+def test_split_schedule_block_sparse_256k():
+    """An all-Block-Sparse layer at 256K (8 query heads, 2 kv heads, top 100:
+    the split schedule with long rows): outputs bit-identical to the joint
+    schedule on the same lists stored with a larger capacity, and sampled
+    query blocks against the oracle fed those lists."""
+    n, hq, hkv, d, top = 262144, 8, 2, 128, 100
+    nb = n // 64
+    say(f"split schedule, block-sparse {n // 1024}K")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q = torch.randn(1, hq, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    k = torch.randn(1, hkv, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    v = torch.randn(1, hkv, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    pat = [W.BSPARSE] * hq
+    bidx, bcnt, _ = mi.block_estimate(q, k, list(range(hq)), top, return_scores=False)
+    idx = mi.build_index(q, k, pat, None, None, bidx, bcnt, top)
+    assert 4 * idx.block_cap <= nb
+    o1, l1 = mi.sparse_prefill(q, k, v, pat, idx, schedule=True)
+    big = mi.alloc_index(1, hq, n, nb // 4 + 1, 1, "cuda")  # a capacity too large for the split
+    big.block_count.copy_(idx.block_count)
+    big.block_idx.fill_(-1)
+    big.block_idx[..., :idx.block_cap].copy_(idx.block_idx)
+    assert 4 * big.block_cap > nb
+    o2, l2 = mi.sparse_prefill(q, k, v, pat, big, schedule=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    q64, k64, v64 = (t[0].double().cpu().numpy() for t in (q, k, v))
+    of, lf = o1[0].double().cpu().numpy(), l1[0].double().cpu().numpy()
+    for h, a in ((0, 0), (3, 1), (5, nb // 2), (7, nb - 1), (6, 2047)):
+        blocks, cols = gpu_index_lists(idx, 0, h, a)
+        ref, rlse = O.attention_from_index(q64[h], k64[h // 4], v64[h // 4], d ** -0.5, a, blocks, cols)
+        rows = slice(64 * a, 64 * a + 64)
+        assert np.abs(of[h, rows] - ref).max() < BF16_ATOL, (h, a)
+        assert np.abs(lf[h, rows] - rlse).max() < 1e-3, (h, a)
 
 
 @pytest.mark.timeout(600)
