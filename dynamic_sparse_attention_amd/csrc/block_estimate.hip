@@ -6,8 +6,8 @@
 //   1. pool:   fp32 means of the 64 rows of every query block of the listed
 //              heads and every key block of their kv heads (HBM-bound read of
 //              Q and K once, 16-byte loads);
-//   2. scores: z[a][c] = scale * Qbar_a . Kbar_c for c <= a, fp32 FMA from
-//              LDS;
+//   2. scores: z[a][c] = scale * Qbar_a . Kbar_c for c <= a, fp32 matrix-core
+//              products;
 //   3. select: per query block a, softmax over c <= a (the block-level
 //              attention weights, formed in registers or LDS and written out
 //              only when the caller asks for them), then the exact top-k by
@@ -110,57 +110,94 @@ __global__ void __launch_bounds__(kPoolNT) bs_pool(BsP p) {
     }
 }
 
-// Lower-triangle 64x64 tiles of z; thread (ty, tx) computes rows 4ty.., cols 4tx..
+// Lower-triangle 128x128 tiles of z.  Each of the four wavefronts computes a
+// 64x64 quarter (wavefront w: rows 64 (w/2), columns 64 (w%2); the quarter
+// above the diagonal of a diagonal tile is skipped) as 4x4 blocks of
+// v_mfma_f32_16x16x4_f32 products (lane l: A = pooled query row l%16 of its
+// block, B = pooled key row l%16, D[4 (l/16) + r][l%16]) with operands read
+// straight from the pooled rows, which stay in L2.  The dimensions are summed
+// in a permuted order so that a lane's operands of four consecutive products
+// are one 16-byte load: product s of dimension group m takes dimension
+// 16 m + 4 (l/16) + s, for A and B alike.  The next group's operands are
+// loaded while the current group's 64 products run.
+constexpr int kScTile = 128;
+
+template <int D>
 __global__ void __launch_bounds__(256) bs_scores(BsP p) {
-    constexpr int KC = 32;
-    __shared__ float qs[64][KC + 1];
-    __shared__ float ks[64][KC + 1];
-    const int T = (p.nb + 63) / 64;
+    const int T = (p.nb + kScTile - 1) / kScTile;
     const int per = T * (T + 1) / 2;
     const int bl = blockIdx.x / per;
     int x = blockIdx.x % per;
     int ta = 0;
     while (x >= ta + 1) { x -= ta + 1; ++ta; }
     const int tc = x;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wv >> 1, wc = wv & 1;
+    if (ta == tc && wc > wr) return;  // every entry above the diagonal
     const int b = bl / p.n_heads, li = bl % p.n_heads;
     const int kslot = p.kvslot[p.heads[li] / p.group];
-    const float* Q = p.qbar + (int64_t)bl * p.nb * p.D;
-    const float* K = p.kbar + ((int64_t)b * p.n_kv + kslot) * p.nb * p.D;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < p.D; k0 += KC) {
-        for (int e = threadIdx.x; e < 64 * KC; e += 256) {
-            const int rr = e / KC, cc = e % KC;
-            const int ar = ta * 64 + rr, cr = tc * 64 + rr;
-            qs[rr][cc] = ar < p.nb ? Q[(int64_t)ar * p.D + k0 + cc] : 0.f;
-            ks[rr][cc] = cr < p.nb ? K[(int64_t)cr * p.D + k0 + cc] : 0.f;
+    const float* Q = p.qbar + (int64_t)bl * p.nb * D;
+    const float* K = p.kbar + ((int64_t)b * p.n_kv + kslot) * p.nb * D;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int row0 = ta * kScTile + 64 * wr, col0 = tc * kScTile + 64 * wc;
+    const float* qp[4];
+    const float* kp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // rows past nb read the last row; their products are not stored
+        qp[i] = Q + (int64_t)min(row0 + 16 * i + r16, p.nb - 1) * D + 4 * g;
+        kp[i] = K + (int64_t)min(col0 + 16 * i + r16, p.nb - 1) * D + 4 * g;
+    }
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 qa[4], kb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qa[i] = *reinterpret_cast<const f32x4*>(qp[i]);
+        kb[i] = *reinterpret_cast<const f32x4*>(kp[i]);
+    }
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        f32x4 qn[4], kn[4];
+        if (m + 1 < D / 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qn[i] = *reinterpret_cast<const f32x4*>(qp[i] + 16 * (m + 1));
+                kn[i] = *reinterpret_cast<const f32x4*>(kp[i] + 16 * (m + 1));
+            }
         }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < KC; ++kk) {
-            float qa[4], kc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) qa[i] = qs[ty * 4 + i][kk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kc[j] = ks[tx * 4 + j][kk];
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(qa[i], kc[j], acc[i][j]);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][s], kb[j][s], acc[i][j], 0, 0, 0);
+        if (m + 1 < D / 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qa[i] = qn[i];
+                kb[i] = kn[i];
+            }
         }
-        __syncthreads();
     }
     float* W = p.w + b * p.w_b + (int64_t)(p.w_by_head ? p.heads[li] : li) * p.w_h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int a = ta * 64 + ty * 4 + i;
-        if (a >= p.nb) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tc * 64 + tx * 4 + j;
-            if (c <= a) W[(int64_t)a * p.nb + c] = acc[i][j] * p.scale;
+        for (int r = 0; r < 4; ++r) {
+            const int a = row0 + 16 * i + 4 * g + r;
+            if (a >= p.nb) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = col0 + 16 * j + r16;
+                if (c <= a) W[(int64_t)a * p.nb + c] = acc[i][j][r] * p.scale;
+            }
         }
-    }
 }
 
 constexpr int kSelNT = 256;
@@ -213,10 +250,11 @@ __global__ void __launch_bounds__(kSelNT) bs_select(BsP p) {
         sum += e;
     }
     sum = block_reduce(sum, red, false);
+    const float inv = 1.f / sum;
     for (int c = threadIdx.x; c < p.nb; c += kSelNT) {
         float wv = 0.f;
         if (c < n) {
-            wv = row[c] / sum;
+            wv = row[c] * inv;
             row[c] = wv;
         }
         if constexpr (WEIGHTS) W[c] = wv;
@@ -355,10 +393,11 @@ __device__ __forceinline__ void wave_weights(float (&x)[R], int n, int nb, float
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const float inv = 1.f / sum;  // one division per row; weights within an ulp of x / sum
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         const int c = lane + 64 * u;
-        x[u] = c < n ? x[u] / sum : 0.f;
+        x[u] = c < n ? x[u] * inv : 0.f;
         if constexpr (WEIGHTS) {
             if (c < nb) W[c] = x[u];
         }
@@ -857,8 +896,10 @@ hipError_t launch_block_estimate(const BsArgs& a, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    const int T = (p.nb + 63) / 64;
-    hipLaunchKernelGGL(bs_scores, dim3(a.B * a.n_heads * (T * (T + 1) / 2)), dim3(256), 0, s, p);
+    const int T = (p.nb + kScTile - 1) / kScTile;
+    const dim3 sgrid((unsigned)(a.B * a.n_heads * (T * (T + 1) / 2))), sblock(256);
+    if (a.D == 64) hipLaunchKernelGGL((bs_scores<64>), sgrid, sblock, 0, s, p);
+    else hipLaunchKernelGGL((bs_scores<128>), sgrid, sblock, 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_select(p, weights, s);
