@@ -276,9 +276,20 @@ __global__ void __launch_bounds__(kSelNT) bs_select(BsP p) {
 // bin), else from a 4-pass radix select over 8-bit digits with the
 // wavefront's 256-bin LDS histogram `hw`; then one ordered ballot pass
 // (slots in index order) writes the list.  No workgroup barriers.
+//
+// Longer rows with k <= kFilterK first filter: the k-th largest T' of the
+// 128 per-lane top-2 keys has at least k keys of the row at or above it (they
+// come from distinct slots), so T >= T'; the keys >= T' (about 120-170 on rows
+// of thousands of blocks) are compacted in index order into the wavefront's
+// LDS buffer `cb` (kSurvCap keys, then their blocks), where the bisection and
+// the ordered pass run over at most kSurvCap / 64 slots.  More survivors
+// (heavy exact ties) take the radix select.
+constexpr int kFilterK = 128;
+constexpr int kSurvCap = 512;
+
 template <int R>
 __device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int n, int top, int32_t* out,
-                                            int32_t* count, uint32_t* hw, int lane) {
+                                            int32_t* count, uint32_t* hw, int lane, uint32_t* cb = nullptr) {
     const int k = min(top, n);
     if (lane == 0) *count = k;
     for (int m = k + lane; m < top; m += 64) out[m] = -1;
@@ -311,6 +322,68 @@ __device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int n, int
         for (int u = 0; u < R; ++u) gt += __popcll(__ballot(key[u] > T));
         need = k - gt;
     } else {
+    if (k <= kFilterK) {
+        uint32_t m1 = 0u, m2 = 0u;  // the lane's two largest keys (absent keys are 0)
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            m2 = max(m2, min(m1, key[u]));
+            m1 = max(m1, key[u]);
+        }
+        uint32_t t = 0u;
+#pragma unroll 1
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            if (__popcll(__ballot(m1 >= cand)) + __popcll(__ballot(m2 >= cand)) >= k) t = cand;
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = lane + 64 * u;
+            const bool sv = c < n && key[u] >= t;
+            const uint64_t m = __ballot(sv);
+            const int pos = cnt + __popcll(m & below);
+            if (sv && pos < kSurvCap) {
+                cb[pos] = key[u];
+                cb[kSurvCap + pos] = (uint32_t)c;
+            }
+            cnt += __popcll(m);
+        }
+        if (cnt <= kSurvCap) {
+            __builtin_amdgcn_wave_barrier();
+            constexpr int V = kSurvCap / 64;
+            uint32_t y[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) y[v] = lane + 64 * v < cnt ? cb[lane + 64 * v] : 0u;
+            uint32_t T = 0u;
+#pragma unroll 1
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                int ge = 0;
+#pragma unroll
+                for (int v = 0; v < V; ++v) ge += __popcll(__ballot(y[v] >= cand));  // absent slots are 0
+                if (ge >= k) T = cand;
+            }
+            int gt = 0;
+#pragma unroll
+            for (int v = 0; v < V; ++v) gt += __popcll(__ballot(y[v] > T));
+            const int need = k - gt;
+            // ordered output over the survivors (their positions follow the blocks' order)
+            int run_eq = 0, run_sel = 0;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int j = lane + 64 * v;
+                const bool g = j < cnt && y[v] > T;
+                const bool e = j < cnt && y[v] == T;
+                const uint64_t me = __ballot(e);
+                const bool sel = g || (e && run_eq + __popcll(me & below) < need);
+                const uint64_t ms = __ballot(sel);
+                if (sel) out[run_sel + __popcll(ms & below)] = (int32_t)cb[kSurvCap + j];
+                run_eq += __popcll(me);
+                run_sel += __popcll(ms);
+            }
+            return;
+        }
+    }
     uint32_t prefix = 0, pmask = 0;
     int rem = k;
 #pragma unroll 1
@@ -411,6 +484,7 @@ constexpr int kWaveRows = 4;  // wavefronts (rows) per workgroup
 template <int R, bool WEIGHTS>
 __global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
     __shared__ uint32_t hist[kWaveRows][256];
+    __shared__ uint32_t surv[kWaveRows][R > 8 ? 2 * kSurvCap : 1];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t rowid = (int64_t)blockIdx.x * kWaveRows + wv;
     if (rowid >= (int64_t)p.B * p.n_heads * p.nb) return;
@@ -434,7 +508,7 @@ __global__ void __launch_bounds__(64 * kWaveRows) bs_select_wave(BsP p) {
         key[u] = c < n ? block_key(x[u], c, a) : 0u;
     }
     const int64_t row = ((int64_t)b * p.Hq + h) * p.nb + a;
-    wave_select<R>(key, n, p.top, p.block_idx + row * p.top, p.block_count + row, hist[wv], lane);
+    wave_select<R>(key, n, p.top, p.block_idx + row * p.top, p.block_count + row, hist[wv], lane, surv[wv]);
 }
 
 // Fused scores and selection for rows of at most kFusedMaxNb blocks: one

@@ -254,6 +254,35 @@ def test_block_estimate_long_rows(nb):
         check_selection(bidx[0, 0, a], w[0, 0, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks a{a}")
 
 
+@pytest.mark.parametrize("nb,top,const", [(1500, 200, False), (2049, 129, False), (4096, 128, False),
+                                          (2049, 20, True), (700, 100, True)])
+def test_block_estimate_long_rows_selection_routes(nb, top, const):
+    """Rows above 512 blocks take one of three selection routes: the filter
+    (survivors of the per-lane top-2 threshold, k <= 128), the radix select
+    (k > 128), and the radix select again when exact ties leave more
+    survivors than the filter's buffer holds (constant inputs: every weight
+    of a row equal, so the lowest blocks are kept).  Every row is checked."""
+    say(f"block_estimate routes nb={nb} top={top} const={const}")
+    n, d = 64 * nb, 64
+    if const:
+        qn = np.full((1, 1, n, d), 0.25, np.float32)
+        q = to_device(qn, "f32")
+        k = to_device(qn.copy(), "f32")
+        q64 = k64 = qn.astype(np.float64)
+    else:
+        _, (q, k, _), (q64, k64, _) = _inputs(19, 1, 1, n, d, "bf16")
+    bidx, bcnt, w = mi.block_estimate(q, k, [0], top)
+    torch.cuda.synchronize()
+    bidx, bcnt, w = bidx.cpu().numpy(), bcnt.cpu().numpy(), f64(w)
+    rw, _ = O.bs_estimate(q64[0, 0], k64[0, 0], d ** -0.5, top)
+    tri = np.tril(np.ones((nb, nb), bool))
+    assert_scores_close(w[0, 0][tri], rw[tri], "block weights")
+    for a in range(nb):
+        kk = min(top, a + 1)
+        assert bcnt[0, 0, a] == kk
+        check_selection(bidx[0, 0, a], w[0, 0, a, : a + 1], rw[a, : a + 1], kk, {0, a}, f"blocks a{a}")
+
+
 # ----------------------------------------------------------------- index building
 
 @pytest.mark.parametrize("n,nv,ns", [(64 * 23, 40, 60), (64 * 8, 600, 600), (64 * 40, 5, 1)])
