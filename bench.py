@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
+    ap.add_argument("--gather-only", action="store_true",
+                    help="only the isolated column-gather measurement on the workload's inputs "
+                         "(eight attention launches: four with the column index, four without columns)")
     return ap.parse_args()
 
 
@@ -583,6 +586,35 @@ def exact_summary(r, d):
             "effective_tflops": round(4.0 * d * r["exact_pairs"] / (r["att_ms"] * 1e-3) / 1e12, 2)}
 
 
+def gather_hbm(workload: str):
+    """HBM bytes and rate of the column gather from a current rocprofv3
+    record (FETCH_SIZE + WRITE_SIZE of the column launches minus those of
+    the launches without columns), or None."""
+    from dynamic_sparse_attention_amd import profile_tables
+    rec = profile_tables.current_gather_record(workload)
+    if rec is None:
+        return None
+    g = rec["gather"]
+    return {k: g[k] for k in ("hbm_bytes", "time_us", "hbm_GBps", "hbm_pct", "staged_GBps", "staged_pct")}
+
+
+def gather_only(w):
+    """The isolated column gather alone on the workload's inputs (for the
+    rocprofv3 passes that measure its HBM bytes): one JSON line."""
+    import torch
+    import workloads as W
+    if w.dtype != "bf16":
+        raise SystemExit("the gather measurement takes a bf16 workload")
+    log(f"[bench] generating {w.name} (N={w.seq_len}) for the gather measurement")
+    data = W.generate(w)
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(data["q"]), up(data["k"]), up(data["v"])
+    del data
+    log("[bench] column gather rate")
+    print(json.dumps({"workload": w.name, "gather": gather_rate(q, k, v, w)}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -596,6 +628,9 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.config]
+    if args.gather_only:
+        gather_only(w)
+        return
     r, plan, data = measure(w, args.steps, args.warmup, not args.no_dense, keep=not args.no_cpu_baseline)
     d = w.head_dim
     achieved = r["flop"] / (r["att_ms"] * 1e-3) / 1e12
@@ -644,6 +679,7 @@ def main():
     if not args.no_gather and w.seq_len >= 65536 and w.dtype == "bf16":
         log("[bench] column gather rate")
         out["gather"] = gather_rate(plan.q, plan.k, plan.v, w)
+        out["gather"]["measured_hbm"] = gather_hbm(w.name)
     if not args.no_antidiag:
         log("[bench] antidiagonal block estimate")
         out["antidiag_estimate"] = antidiag_rate(plan.q, plan.k, w)

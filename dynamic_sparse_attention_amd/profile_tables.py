@@ -276,6 +276,133 @@ def markdown(rec: dict, title: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+# ----------------------------------------------------------------------------
+# The column gather: per-dispatch values of the isolated gather measurement
+# ----------------------------------------------------------------------------
+
+ATTN = "sparse_attn_kernel"
+
+
+def attn_dispatch_times(run_dir: str) -> list:
+    """Durations (us) of the attention dispatches of a kernel trace, in dispatch order."""
+    rows = []
+    with open(_one("*kernel_trace.csv", run_dir)) as fh:
+        for row in csv.DictReader(fh):
+            if short_name(row["Kernel_Name"]).startswith(ATTN):
+                rows.append((int(row["Dispatch_Id"]),
+                             (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3))
+    return [t for _, t in sorted(rows)]
+
+
+def attn_dispatch_counter(run_dir: str, counter: str) -> list:
+    """A counter's value (KiB) per attention dispatch of a --pmc run, in dispatch order."""
+    rows = defaultdict(float)
+    with open(_one("*counter_collection.csv", run_dir)) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] == counter and short_name(row["Kernel_Name"]).startswith(ATTN):
+                rows[int(row["Dispatch_Id"])] += float(row["Counter_Value"])
+    return [rows[k] for k in sorted(rows)]
+
+
+def _median(x):
+    x = sorted(x)
+    n = len(x)
+    return x[n // 2] if n % 2 else 0.5 * (x[n // 2 - 1] + x[n // 2])
+
+
+def build_gather_record(args) -> dict:
+    """The gather launch sequence of ``bench.py --gather-only``: one warmup and
+    three timed attention launches with the column index, then the same
+    without columns.  The gather's time and HBM bytes are the differences of
+    the two groups (median of the timed launches; counters scaled by the
+    copy calibration)."""
+    times = attn_dispatch_times(args.trace)
+    fetch = attn_dispatch_counter(args.fetch, "FETCH_SIZE")
+    write = attn_dispatch_counter(args.write, "WRITE_SIZE")
+    for what, xs in (("trace", times), ("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        if len(xs) != 8:
+            raise ValueError(f"{what}: expected 8 attention dispatches, found {len(xs)}")
+    ff, fraw = copy_factor(args.copy_fetch, "FETCH_SIZE")
+    wf, wraw = copy_factor(args.copy_write, "WRITE_SIZE")
+    bench = {}
+    if args.bench_log and os.path.exists(args.bench_log):
+        with open(args.bench_log) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    bench = json.loads(line)["gather"]
+    groups = {}
+    for name, sl in (("columns", slice(1, 4)), ("diagonal_only", slice(5, 8))):
+        f = _median(fetch[sl]) * 1024.0 * ff
+        wb = _median(write[sl]) * 1024.0 * wf
+        groups[name] = {"avg_us": round(_median(times[sl]), 2), "fetch_bytes": round(f), "write_bytes": round(wb)}
+    c, d0 = groups["columns"], groups["diagonal_only"]
+    t_us = c["avg_us"] - d0["avg_us"]
+    hbm = (c["fetch_bytes"] + c["write_bytes"]) - (d0["fetch_bytes"] + d0["write_bytes"])
+    staged = float(bench.get("bytes", 0))
+    g = {"time_us": round(t_us, 2), "hbm_bytes": round(hbm),
+         "hbm_GBps": round(hbm / (t_us * 1e3), 1), "hbm_pct": round(100.0 * hbm / (t_us * 1e3) / PEAK_HBM_GBS, 1),
+         "staged_bytes": round(staged), "columns": bench.get("columns"),
+         "staged_GBps": round(staged / (t_us * 1e3), 1) if staged else None,
+         "staged_pct": round(100.0 * staged / (t_us * 1e3) / PEAK_HBM_GBS, 1) if staged else None}
+    return {"workload": bench_workload(args.workload), "kernel_source_sha256": source_sha256(),
+            "command": args.command, "fetch_scale": ff, "write_scale": wf,
+            "copy_fetch_kib": fraw, "copy_write_kib": wraw, "launches": groups, "gather": g}
+
+
+def bench_workload(key: str) -> str:
+    import workloads as W
+    return W.WORKLOADS[key].name
+
+
+def gather_markdown(rec: dict) -> str:
+    g, L = rec["gather"], rec["launches"]
+    lines = [f"# Column gather: HBM bytes and rate ({rec['workload']})", "",
+             f"Kernel sources (csrc/, SHA-256): `{rec['kernel_source_sha256']}`", "",
+             "Command (its rocprofv3 passes run from /tmp with TMPDIR=/tmp; OUT = an output folder):", "",
+             "```", rec["command"], "```", "",
+             "The isolated gather of `bench.py --gather-only`: the layer's Q/K/V with a column-only index (slash set "
+             "{0}: each query block computes its diagonal tile only, plus up to 1000 gathered key columns per head), "
+             "one warmup and three timed attention launches, then the same launches without columns. The gather's "
+             "time and HBM bytes are the differences of the two groups (medians of the timed launches). "
+             f"FETCH_SIZE is scaled by {rec['fetch_scale']:.4f} and WRITE_SIZE by {rec['write_scale']:.4f} "
+             "(a device copy that reads and writes 1 GiB). The algorithmic bytes of the gather are the gathered "
+             "K and V rows staged into LDS (2 d x 2 bytes per column per query block); a row that several query "
+             "blocks gather, or that is still in L2/MALL, is staged each time but fetched from HBM once, so the "
+             "measured HBM bytes can be far below them.", "",
+             "| launches | average us | HBM read MB | HBM written MB |", "|---|---|---|---|"]
+    for name in ("columns", "diagonal_only"):
+        x = L[name]
+        lines.append(f"| {name.replace('_', ' ')} | {x['avg_us']:.1f} | {x['fetch_bytes'] / 1e6:.1f} | "
+                     f"{x['write_bytes'] / 1e6:.1f} |")
+    lines += ["", "| gather | value |", "|---|---|",
+              f"| time the columns add | {g['time_us']:.1f} us |",
+              f"| columns gathered (per query block, summed) | {g['columns']} |",
+              f"| HBM bytes the columns add | {g['hbm_bytes'] / 1e6:.1f} MB |",
+              f"| HBM rate | {g['hbm_GBps']:.0f} GB/s, {g['hbm_pct']:.1f}% of 8 TB/s |",
+              f"| algorithmic bytes (K and V rows staged into LDS) | {g['staged_bytes'] / 1e6:.1f} MB |",
+              f"| algorithmic rate | {g['staged_GBps']:.0f} GB/s, {g['staged_pct']:.1f}% of 8 TB/s |",
+              f"| share of the staged rows fetched from HBM | "
+              f"{100.0 * g['hbm_bytes'] / max(g['staged_bytes'], 1):.1f}% |", ""]
+    return "\n".join(lines)
+
+
+def gather_record_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gather_{workload_name}.json")
+
+
+def current_gather_record(workload_name: str):
+    """The committed gather record for a workload if it was taken on the
+    current kernel sources, else None."""
+    p = gather_record_path(workload_name)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256") != source_sha256():
+        return None
+    return rec
+
+
 def record_path(workload_name: str) -> str:
     return os.path.join(ROOT, "profiles", f"layer_kernels_{workload_name}.json")
 
@@ -307,7 +434,18 @@ def main(argv=None):
     ap.add_argument("--command", default="")
     ap.add_argument("--title", default=None)
     ap.add_argument("--out", default=None, help="output path without extension (default profiles/layer_kernels_<name>)")
+    ap.add_argument("--gather", action="store_true",
+                    help="the runs are of bench.py --gather-only: write profiles/gather_<name>")
     args = ap.parse_args(argv)
+    if args.gather:
+        rec = build_gather_record(args)
+        out = args.out or os.path.splitext(gather_record_path(rec["workload"]))[0]
+        with open(out + ".json", "w") as fh:
+            json.dump(rec, fh, indent=1)
+        with open(out + ".md", "w") as fh:
+            fh.write(gather_markdown(rec))
+        print(out + ".md")
+        return
     rec = build_record(args)
     out = args.out or os.path.splitext(record_path(rec["workload"]))[0]
     import workloads as W

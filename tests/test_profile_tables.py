@@ -78,3 +78,51 @@ def test_committed_records_name_their_workload():
             rec = json.load(open(os.path.join(d, f)))
             assert rec["workload"] in names
             assert len(rec["kernel_source_sha256"]) == 64
+
+
+def test_gather_record_takes_the_difference_of_the_two_launch_groups(tmp_path):
+    """bench.py --gather-only launches the attention eight times: one warmup
+    and three timed with the column index, then the same without columns;
+    the gather's time and HBM bytes are the differences of the medians of
+    the timed launches, with the counters scaled by the copy calibration."""
+    att = "void mi::(anonymous namespace)::sparse_attn_kernel<unsigned short, 128, false, false>(P)"
+    other = "mi::(anonymous namespace)::build_index_kernel(P)"
+    (tmp_path / "trace").mkdir()
+    with open(tmp_path / "trace" / "t_kernel_trace.csv", "w") as fh:
+        fh.write('"Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        durs = [9e6, 5e6, 5.2e6, 4.8e6, 3e6, 2e6, 2.1e6, 1.9e6]  # ns: warmup, timed x3; twice
+        t = 0
+        for i, dn in enumerate(durs):
+            fh.write(f'{2 * i},"{other}",{t},{t + 1000}\n')
+            fh.write(f'{2 * i + 1},"{att}",{t + 2000},{t + 2000 + int(dn)}\n')
+            t += 10 ** 8
+    fetch = [50.0, 40.0, 41.0, 39.0, 20.0, 10.0, 10.0, 10.0]  # KiB
+    write = [8.0, 6.0, 6.0, 6.0, 6.0, 5.0, 5.0, 5.0]
+    _pmc(tmp_path / "fetch", [(n, "FETCH_SIZE", v) for i, v in enumerate(fetch) for n in (other, att)])
+    _pmc(tmp_path / "write", [(n, "WRITE_SIZE", v) for i, v in enumerate(write) for n in (other, att)])
+    copy = "void at::native::copy_kernel(int)"
+    _pmc(tmp_path / "cf", [(copy, "FETCH_SIZE", (1 << 20) / 2)])
+    _pmc(tmp_path / "cw", [(copy, "WRITE_SIZE", 1 << 20)])
+    log = tmp_path / "bench.log"
+    log.write_text('[bench] column gather rate\n{"workload": "x", "gather": {"columns": 7, "bytes": 9000000}}\n')
+
+    class A:
+        workload, steps, command = "c3", 8, "cmd"
+        trace, fetch, write = str(tmp_path / "trace"), str(tmp_path / "fetch"), str(tmp_path / "write")
+        copy_fetch, copy_write, bench_log = str(tmp_path / "cf"), str(tmp_path / "cw"), str(log)
+    rec = P.build_gather_record(A)
+    assert rec["launches"]["columns"]["avg_us"] == pytest.approx(5000.0)
+    assert rec["launches"]["diagonal_only"]["avg_us"] == pytest.approx(2000.0)
+    g = rec["gather"]
+    assert g["time_us"] == pytest.approx(3000.0)
+    # FETCH medians 40 and 10 KiB (x 2), WRITE 6 and 5 KiB (x 1)
+    assert g["hbm_bytes"] == (40 - 10) * 2 * 1024 + (6 - 5) * 1024
+    assert g["hbm_GBps"] == pytest.approx(g["hbm_bytes"] / 3e6, abs=0.1)
+    assert g["staged_bytes"] == 9000000 and g["columns"] == 7
+    assert g["staged_GBps"] == pytest.approx(3.0)  # 9 MB in 3 ms
+    assert rec["workload"] == W.C3.name
+    assert "Column gather" in P.gather_markdown(rec)
+    # a run that lost a launch is refused
+    _pmc(tmp_path / "write", [(att, "WRITE_SIZE", v) for v in write[:7]])
+    with pytest.raises(ValueError):
+        P.build_gather_record(A)
