@@ -77,3 +77,26 @@ def test_plant_recall_counts_planted_keys_and_hot_blocks():
     plan = types.SimpleNamespace(pat=[W.VSLASH] * w3.heads_q, vidx=torch.from_numpy(vidx), bidx=None, bcnt=None)
     r = bench.plant_recall(plan, w3)["vertical"]
     assert r["mean_recall"] == r["min_recall"] == r["max_recall"] == 0.5
+
+
+def test_gather_hbm_reports_a_current_record_only(monkeypatch):
+    """bench.py reports the gather's counter-measured HBM bytes only from a
+    record taken on the current kernel sources."""
+    from dynamic_sparse_attention_amd import profile_tables as P
+    g = {"hbm_bytes": 6, "time_us": 3.0, "hbm_GBps": 2.0, "hbm_pct": 0.1, "staged_GBps": 5.0, "staged_pct": 0.2,
+         "columns": 7, "staged_bytes": 15}
+    monkeypatch.setattr(P, "current_gather_record", lambda name: {"gather": g} if name == "w" else None)
+    assert bench.gather_hbm("w") == {k: g[k] for k in ("hbm_bytes", "time_us", "hbm_GBps", "hbm_pct",
+                                                       "staged_GBps", "staged_pct")}
+    assert bench.gather_hbm("other") is None
+
+
+def test_committed_profiles_are_current():
+    """The committed rocprofv3 tables (the four layers and the gather) were
+    taken on the committed kernel sources: a kernel change without new
+    profiles fails here."""
+    from dynamic_sparse_attention_amd import profile_tables as P
+    rec = P.current_gather_record(W.C3.name)
+    assert rec is not None and rec["gather"]["hbm_bytes"] > 0 and rec["gather"]["staged_bytes"] > 0
+    for w in (W.C2, W.C3, W.C4, W.C5):
+        assert P.current_record(w.name) is not None, w.name
